@@ -1,0 +1,73 @@
+"""Norms, the Cauchy-Schwarz row bound and per-head eligibility, in fp64.
+
+TEST INFRASTRUCTURE (see the package header): never imported by the product.
+
+Source: vatt-ghern "deep-heygen-avatar-iv-trillium-tpu", section
+拿掉 softmax 的序列相依.  A logit q.k can never exceed |q| |k| (Cauchy-Schwarz),
+so ``m_i = scale * |q_i| * max over attended keys |k_j|`` bounds every score of
+row i before any score is computed; precomputed norms are handed to the kernel
+so each row knows its bound up front.  The bound is not tight for every head:
+eligibility is decided per head, and ineligible heads use the online max.
+
+Readings where the pages leave the step open (each listed in the design notes):
+
+* The maximum key norm is taken over all keys the row attends (one fixed
+  shift per row).  A per-block maximum would change the shift from block to
+  block and bring the rescaling back.
+* Eligibility is a norm-only sufficient condition: since
+  ``-m_i <= max_j s_ij <= m_i``, the slack ``m_i - max_j s_ij`` is at most
+  ``2 m_i <= 2 * scale * max_n |q_n| * max_n |k_n|``.  A head is eligible when
+  that head-wide quantity is at most 60 (nats), inclusive: then the largest
+  term ``exp(s - m)`` is at least ``e^-60``, 27 nats above the smallest normal
+  float32/bf16 value ``e^-87.3``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import frame_mask, widen
+
+GRANULE = 16
+ELIGIBLE_NATS = 60.0
+
+
+def row_norms(x):
+    """``|x_n|_2`` per row, fp64, ``[B, H, N]``."""
+    x = widen(x)
+    return np.sqrt((x * x).sum(axis=-1))
+
+
+def granule_max(knorm):
+    """Max key norm over each 16-key granule: ``[B, H, N] -> [B, H, N/16]``."""
+    B, H, N = knorm.shape
+    return knorm.reshape(B, H, N // GRANULE, GRANULE).max(axis=-1)
+
+
+def head_max(qnorm, knorm):
+    """``[B, H, 2]``: (max_n |q_n|, max_n |k_n|)."""
+    return np.stack([qnorm.max(axis=-1), knorm.max(axis=-1)], axis=-1)
+
+
+def row_bound(q, k, pattern, scale, rows=None):
+    """``m_i = scale |q_i| max_{j attended by i} |k_j|`` in fp64, ``[B, H, R]``."""
+    qn = row_norms(q)
+    kn = row_norms(k)
+    B, H, N = qn.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    M = frame_mask(pattern, rows, N)
+    out = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            kmax = np.where(M, kn[b, h][None, :], -np.inf).max(axis=1)
+            out[b, h] = scale * qn[b, h, rows] * kmax
+    return out
+
+
+def slack_bound(hmax, scale):
+    """Head-wide upper bound on the slack: ``2 scale max|q| max|k|`` (nats), ``[B, H]``."""
+    return 2.0 * scale * hmax[..., 0] * hmax[..., 1]
+
+
+def eligible(hmax, scale, limit=ELIGIBLE_NATS):
+    """Per-head eligibility for the bound softmax, ``[B, H]`` bool (inclusive)."""
+    return slack_bound(hmax, scale) <= limit

@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs shaped like the video-chunk attention workloads.
+
+This module only *creates inputs*: workload shapes, frame-window patterns and
+seeded bf16 Q/K/V tensors. It holds none of the attention arithmetic, so both
+the CPU oracle (``oracle/``) and the HIP path (``block_sparse_video_frame_amd``)
+may import it without sharing any of the method's code.
+
+Workloads (token layout is frame by frame: token ``n = f*T + t``):
+
+=========  ======  =====  ====  ==================  ==========================
+name       batch   heads  D     frames x tokens     pattern
+=========  ======  =====  ====  ==================  ==========================
+tiny       1       2      64    4 x 48   (N 192)    +-1 frame
+720p       1       8      128   13 x 3600 (N 46800) +-1 frame + frame 0 global
+1080p      1       8      128   7 x 8160 (N 57120)  +-1 frame + frame 0 global
+stress     as 720p, rows scaled by log-normal(0, 0.75) norms, 1% of keys x8
+sr         1       16     64    5 x 14400 (N 72000) frame-local
+=========  ======  =====  ====  ==================  ==========================
+
+Recipe: ``numpy.random.default_rng(seed)``; draw ``standard_normal`` float32 in
+the order Q, K, V, each ``[B, H, N, D]`` C-order; round float32 -> bf16 with
+round-to-nearest-even on the bit pattern.  The stress workload draws the same
+Q, K, V first, then ``z_q``, ``z_k`` (``[B, H, N]`` standard normal) and an
+outlier uniform ``[B, H, N]``; each Q row is multiplied by ``exp(0.75 z_q)``,
+each K row by ``exp(0.75 z_k)`` and, where the uniform is below 0.01, by 8;
+all in float32, rounded to bf16 once at the end.  V is left unscaled.
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "Pattern", "Workload", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "make_qkv", "random_qkv", "sha256",
+]
+
+
+@dataclass(frozen=True)
+class Pattern:
+    """Frame-window attention pattern over a frame-major token sequence."""
+    num_frames: int
+    tokens_per_frame: int
+    win_before: int
+    win_after: int
+    global_frames: tuple = field(default_factory=tuple)
+
+    @property
+    def seq_len(self) -> int:
+        return self.num_frames * self.tokens_per_frame
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    pattern: Pattern
+    stress: bool = False
+    seed: int = 0
+
+    @property
+    def seq_len(self) -> int:
+        return self.pattern.seq_len
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(D), as the float32 value both sides use."""
+        return float(np.float32(1.0) / np.sqrt(np.float32(self.head_dim)))
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 64, Pattern(4, 48, 1, 1)),
+    "720p": Workload("720p", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,))),
+    "1080p": Workload("1080p", 1, 8, 128, Pattern(7, 8160, 1, 1, (0,))),
+    "stress": Workload("stress", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), stress=True),
+    "sr": Workload("sr", 1, 16, 64, Pattern(5, 14400, 0, 0)),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest, ties to even); returns uint16 bits.
+
+    NaN is kept quiet NaN; the generators never produce one.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    r = r.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 exactly."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def random_qkv(batch, heads, seq_len, head_dim, seed=0, stress=False):
+    """Seeded bf16 Q, K, V (uint16 bit arrays, ``[B, H, N, D]``)."""
+    rng = np.random.default_rng(seed)
+    shape = (batch, heads, seq_len, head_dim)
+    q = _draw(rng, shape)
+    k = _draw(rng, shape)
+    v = _draw(rng, shape)
+    if stress:
+        rows = (batch, heads, seq_len)
+        zq = _draw(rng, rows)
+        zk = _draw(rng, rows)
+        u = rng.random(size=rows, dtype=np.float32)
+        q *= np.exp(np.float32(0.75) * zq)[..., None]
+        ks = np.exp(np.float32(0.75) * zk)
+        ks = np.where(u < np.float32(0.01), ks * np.float32(8.0), ks).astype(np.float32)
+        k *= ks[..., None]
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def make_qkv(wl: Workload, seed: int | None = None):
+    """Q, K, V bf16 bit arrays for a named workload."""
+    return random_qkv(wl.batch, wl.heads, wl.seq_len, wl.head_dim,
+                      wl.seed if seed is None else seed, wl.stress)
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()

@@ -1,0 +1,205 @@
+"""Pins of the CPU fp64 oracle to things other than itself (runs on CPU).
+
+* brute force: pure-Python loops with math.fsum on the tiny workload;
+* a library routine: torch's scaled_dot_product_attention (fp64, CPU) on the
+  key set gathered by slicing frames, for every pattern kind (window, global
+  frame, frame-local, all frames);
+* closed forms: uniform softmax (LSE = ln of the attended count);
+* invariants: rows of P/l sum to one, the block-by-block evaluation over the
+  attended intervals equals the dense masked one (online and bound shift), the
+  Cauchy-Schwarz bound is never below the true row max.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import blocks as BL
+from oracle import norms as NM
+from synth import WORKLOADS, Pattern, bf16_bits_to_f32, random_qkv
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small(pattern, B=1, H=2, D=32, seed=3, stress=False):
+    return random_qkv(B, H, pattern.seq_len, D, seed=seed, stress=stress)
+
+
+def keys_by_slicing(pattern, f):
+    """Attended key tokens of query frame f, built by slicing whole frames."""
+    T = pattern.tokens_per_frame
+    frames = [g for g in range(pattern.num_frames)
+              if -pattern.win_before <= g - f <= pattern.win_after or g in pattern.global_frames]
+    return np.concatenate([np.arange(g * T, (g + 1) * T) for g in frames])
+
+
+def sdpa_reference(q, k, v, pattern, scale):
+    """Per query frame, torch SDPA (fp64, CPU) on the gathered keys; LSE by torch.logsumexp."""
+    qf = torch.from_numpy(bf16_bits_to_f32(q).astype(np.float64))
+    kf = torch.from_numpy(bf16_bits_to_f32(k).astype(np.float64))
+    vf = torch.from_numpy(bf16_bits_to_f32(v).astype(np.float64))
+    B, H, N, D = qf.shape
+    T = pattern.tokens_per_frame
+    out = torch.empty_like(qf)
+    lse = torch.empty(B, H, N, dtype=torch.float64)
+    for f in range(pattern.num_frames):
+        ks = torch.from_numpy(keys_by_slicing(pattern, f))
+        qs = qf[:, :, f * T:(f + 1) * T]
+        kk = kf[:, :, ks].contiguous()
+        vv = vf[:, :, ks].contiguous()
+        out[:, :, f * T:(f + 1) * T] = torch.nn.functional.scaled_dot_product_attention(qs, kk, vv, scale=scale)
+        lse[:, :, f * T:(f + 1) * T] = torch.logsumexp(scale * qs @ kk.transpose(-1, -2), dim=-1)
+    return out.numpy(), lse.numpy()
+
+
+def test_brute_force_tiny():
+    wl = WORKLOADS["tiny"]
+    q, k, v = random_qkv(wl.batch, wl.heads, wl.seq_len, wl.head_dim, seed=0)
+    O, L = A.attention(q, k, v, wl.pattern, wl.scale)
+    Ob, Lb = A.brute_force(q, k, v, wl.pattern, wl.scale)
+    assert np.abs(O - np.array(Ob)).max() <= 1e-12
+    assert np.abs(L - np.array(Lb)).max() <= 1e-12
+
+
+@pytest.mark.parametrize("pattern", [
+    Pattern(4, 48, 1, 1),            # +-1 window (tiny)
+    Pattern(6, 32, 1, 1, (0,)),      # +-1 window + global frame 0
+    Pattern(5, 32, 0, 0),            # frame-local (block diagonal)
+    Pattern(4, 32, 4, 4),            # every frame sees every frame: plain dense attention
+    Pattern(7, 16, 2, 0, (3, 6)),    # lopsided window, two global frames
+])
+def test_against_sdpa(pattern):
+    q, k, v = small(pattern)
+    scale = 1.0 / math.sqrt(32)
+    O, L = A.attention(q, k, v, pattern, scale, chunk=40)
+    Or, Lr = sdpa_reference(q, k, v, pattern, scale)
+    assert np.abs(O - Or).max() <= 1e-12
+    assert np.abs(L - Lr).max() <= 1e-12
+
+
+def test_dense_whole_sequence_is_sdpa():
+    pattern = Pattern(3, 48, 2, 2)
+    q, k, v = small(pattern, D=64)
+    qf, kf, vf = (torch.from_numpy(bf16_bits_to_f32(x).astype(np.float64)) for x in (q, k, v))
+    O, L = A.attention(q, k, v, pattern, 0.125)
+    Or = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, scale=0.125).numpy()
+    assert np.abs(O - Or).max() <= 1e-12
+
+
+def test_uniform_softmax_closed_form():
+    """Q = 0: every attended score is 0, so softmax is uniform over the attended set."""
+    gold = json.load(open(os.path.join(GOLD, "uniform_lse.json")))
+    wl = WORKLOADS["tiny"]
+    _, k, v = random_qkv(1, 2, wl.seq_len, 64, seed=0)
+    q = np.zeros_like(k)
+    O, L = A.attention(q, k, v, wl.pattern, wl.scale)
+    T = gold["tokens_per_frame"]
+    vf = bf16_bits_to_f32(v).astype(np.float64)
+    for f, (nk, lse) in enumerate(zip(gold["attended_keys_per_frame"], gold["lse_per_frame"])):
+        assert np.abs(L[:, :, f * T:(f + 1) * T] - lse).max() <= 1e-12
+        lo, hi = max(0, f - 1) * T, min(4, f + 2) * T
+        assert hi - lo == nk
+        mean = vf[:, :, lo:hi].mean(axis=2)
+        assert np.abs(O[:, :, f * T:(f + 1) * T] - mean[:, :, None, :]).max() <= 1e-12
+
+
+def test_identical_keys_uniform():
+    """All keys equal: scores of a row are all equal, LSE = s + ln(count)."""
+    pattern = Pattern(5, 32, 1, 1, (0,))
+    q, k, v = small(pattern)
+    k[:] = k[:, :, :1, :]
+    scale = 0.25
+    O, L = A.attention(q, k, v, pattern, scale)
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    kf = bf16_bits_to_f32(k).astype(np.float64)
+    s = scale * (qf * kf[:, :, :1, :]).sum(-1)
+    counts = np.array([2, 3, 4, 4, 3]).repeat(32) * 32
+    assert np.abs(L - (s + np.log(counts))).max() <= 1e-12
+
+
+def test_rows_sum_to_one():
+    pattern = Pattern(6, 32, 1, 1, (0,))
+    q, k, _ = small(pattern, stress=True)
+    ones = np.ones(q.shape)
+    O, _ = A.attention(q, k, ones, pattern, 0.2)
+    assert np.abs(O - 1.0).max() <= 1e-12
+
+
+@pytest.mark.parametrize("pattern,bq", [
+    (Pattern(4, 48, 1, 1), 32),
+    (Pattern(6, 80, 1, 1, (0,)), 64),
+    (Pattern(5, 64, 0, 0), 48),
+    (Pattern(7, 48, 2, 1, (2, 6)), 16),
+])
+def test_blockwise_equals_dense(pattern, bq):
+    q, k, v = small(pattern)
+    scale = 1.0 / math.sqrt(32)
+    blk = BL.derive_blocks(pattern, bq)
+    O, L = A.attention(q, k, v, pattern, scale)
+    Oo, Lo = A.blockwise(q, k, v, blk, scale, "online", block_k=32)
+    assert np.abs(O - Oo).max() <= 1e-12 and np.abs(L - Lo).max() <= 1e-12
+    bound = NM.row_bound(q, k, pattern, scale)
+    Ob, Lb = A.blockwise(q, k, v, blk, scale, "bound", bound=bound, block_k=48)
+    assert np.abs(O - Ob).max() <= 1e-12 and np.abs(L - Lb).max() <= 1e-12
+
+
+def test_bound_shift_equals_online_and_dominates_max():
+    pattern = Pattern(6, 32, 1, 1, (0,))
+    for stress in (False, True):
+        q, k, v = small(pattern, D=64, stress=stress)
+        scale = 0.125
+        bound = NM.row_bound(q, k, pattern, scale)
+        mx = A.scores_max(q, k, pattern, scale)
+        assert (bound >= mx).all()
+        O, L = A.attention(q, k, v, pattern, scale)
+        Ob, Lb, _ = A.attention_shifted(q, k, v, pattern, scale, bound)
+        ok = (bound - mx) < 600.0
+        assert ok.mean() > 0.5
+        assert np.abs(O - Ob)[ok].max() <= 1e-12
+        assert np.abs(L - Lb)[ok].max() <= 1e-12
+
+
+def test_norms_against_definition_by_loops():
+    pattern = Pattern(2, 32, 0, 0)
+    q, k, _ = small(pattern, D=16)
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    kn = NM.row_norms(k)
+    qn = NM.row_norms(q)
+    for b in range(1):
+        for h in range(2):
+            for n in range(0, 64, 7):
+                assert abs(qn[b, h, n] - math.sqrt(math.fsum(x * x for x in qf[b, h, n]))) <= 1e-13
+    g = NM.granule_max(kn)
+    assert g.shape == (1, 2, 4)
+    assert g[0, 1, 2] == max(kn[0, 1, 32:48])
+    hm = NM.head_max(qn, kn)
+    assert hm[0, 0, 0] == qn[0, 0].max() and hm[0, 1, 1] == kn[0, 1].max()
+
+
+def test_eligibility_threshold_is_inclusive():
+    hm = np.array([[[6.0, 5.0], [6.0, 5.0000001]]])
+    e = NM.eligible(hm, 0.5)  # 2 * 0.5 * 6 * 5 = 30
+    assert e.all()
+    e = NM.eligible(hm, 1.0)  # 60 exactly, then just above 60
+    assert e[0, 0] and not e[0, 1]
+
+
+def test_eligibility_on_workload_heads():
+    """The N(0,1) workloads sit far below 60 nats; the stress workload far above."""
+    for name, want in [("tiny", True), ("stress", False)]:
+        wl = WORKLOADS[name]
+        if name == "stress":
+            q, k, _ = random_qkv(1, 1, 3600 * 4, 128, seed=0, stress=True)
+        else:
+            q, k, _ = random_qkv(1, wl.heads, wl.seq_len, wl.head_dim, seed=0)
+        hm = NM.head_max(NM.row_norms(q), NM.row_norms(k))
+        sl = NM.slack_bound(hm, wl.scale)
+        assert (NM.eligible(hm, wl.scale) == want).all(), sl
+        if want:
+            assert (sl < 40.0).all()
+        else:
+            assert (sl > 1000.0).all()
