@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of the frame-aligned block-sparse attention forward on one MI355X.
+
+One step = the whole hot path over one batch of resident synthetic input:
+attn_norms (per-row |q|, per-16-key max |k|, per-head maxima) followed by
+attn_fwd (bound softmax with per-head online fallback, or the online softmax
+for --mode 0).  The block list is built once per pattern (host, integer) and
+uploaded before timing; its host time is reported as ``setup_ms``.
+
+Metric: useful TFLOP/s = 4 * D * (unmasked query-key pairs) * B * H / time.
+Prints one JSON line.  Default workload: the 720p chunk (1 x 8 heads x 128,
+13 frames x 3600 tokens, +-1 frame window + frame 0 global).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_video_frame_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "include", "bsvf.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, mode: int):
+    """HBM bytes per attn_fwd launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != source_hash() or int(d.get("mode", -1)) != mode:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, target_s: float):
+    """The fp64 oracle, timed on a bounded sample of query rows of the workload."""
+    from oracle import attention as OA
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    T = wl.pattern.tokens_per_frame
+    F = wl.pattern.num_frames
+    rng = np.random.default_rng(1)
+
+    def keys_of(row):
+        f = row // T
+        frames = [g for g in range(F) if -wl.pattern.win_before <= g - f <= wl.pattern.win_after
+                  or g in wl.pattern.global_frames]
+        return len(frames) * T
+
+    n = 64
+    spent, useful, rows_done = 0.0, 0.0, 0
+    while spent < target_s:
+        rows = np.sort(rng.choice(wl.seq_len, size=n, replace=False))
+        qh, kh, vh = q[:, :1], k[:, :1], v[:, :1]   # one head
+        t0 = time.perf_counter()
+        OA.attention(qh, kh, vh, wl.pattern, wl.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        spent += dt
+        rows_done += n
+        useful += sum(4.0 * wl.head_dim * keys_of(int(r)) for r in rows)
+        n = int(min(4096, max(64, n * max(1.0, min(4.0, (target_s - spent) / max(dt, 1e-3) / 2)))))
+    return {"value": useful / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} random query rows of head 0 of the {wl.name} workload, "
+                      f"fp64 dense masked attention over all {wl.seq_len} keys, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with fallback, 2 forced bound")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU form (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_video_frame_amd as bs
+    from synth import WORKLOADS, make_qkv
+
+    wl = WORKLOADS[args.workload]
+    B, H, N, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {wl.name}: B{B} H{H} N{N} D{D} mode {args.mode}", file=sys.stderr, flush=True)
+    qb, kb, vb = make_qkv(wl)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(qb), up(kb), up(vb)
+    t0 = time.perf_counter()
+    blocks = bs.build_blocks_for(wl.pattern, bs.MAX_BLOCK_Q)
+    setup_ms = (time.perf_counter() - t0) * 1e3
+    dblk = blocks.to_device(dev, B, H)
+    useful_flop = 4.0 * D * blocks.useful_pairs * B * H
+    qn = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    kg = torch.empty(B, H, N // 16, dtype=torch.float32, device=dev)
+    hm = torch.empty(B, H, 2, dtype=torch.float32, device=dev)
+    o = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    hp = torch.empty(B, H, dtype=torch.int32, device=dev)
+    need_norms = args.mode != bs.SOFTMAX_ONLINE
+
+    def step(ev=None):
+        if need_norms:
+            if ev:
+                ev[0].record()
+            bs.norms(q, k, out=(qn, kg, hm))
+        if ev:
+            ev[1].record()
+        bs.attention(q, k, v, dblk, wl.scale, args.mode, norms=(qn, kg, hm) if need_norms else None,
+                     out=o, lse=lse, head_path=hp)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # Whole-step timing.
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # Per-kernel timing over separate timed steps (events bracket each launch on
+    # the stream the kernels run on).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    norms_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if need_norms else 0.0
+    paths = hp.cpu().tolist()
+    print(f"[bench] step {ms_step:.3f} ms, attn_fwd {fwd_ms:.3f} ms, attn_norms {norms_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    value = useful_flop / (ms_step * 1e-3) / 1e12
+    fwd_tflops = useful_flop / (fwd_ms * 1e-3) / 1e12
+    norms_bytes = 2 * B * H * N * D * 2 + 4 * B * H * (N + N // 16 + 2)
+    traffic = load_traffic(wl.name, args.mode)
+    res = {
+        "metric": "useful TFLOP/s (unmasked blocks) block-sparse attn fwd; % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} chunk: B{B} H{H} D{D}, {wl.pattern.num_frames} frames x "
+                               f"{wl.pattern.tokens_per_frame} tokens (N {N}), window -{wl.pattern.win_before}/"
+                               f"+{wl.pattern.win_after}, global {list(wl.pattern.global_frames)}",
+                   "softmax_mode": args.mode, "block_q": bs.MAX_BLOCK_Q,
+                   "useful_flop": useful_flop, "useful_pairs_per_head": blocks.useful_pairs},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "attn_fwd_ms": round(fwd_ms, 4),
+        "attn_norms_ms": round(norms_ms, 4),
+        "attn_norms_GBs": round(norms_bytes / (norms_ms * 1e-3) / 1e9, 1) if norms_ms else None,
+        "head_paths": paths,
+        "setup_ms": round(setup_ms, 3),
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "attn_fwd",
+                     "per_launch_flop": useful_flop},
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, qb, kb, vb, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+"""Frame-aligned block-sparse video attention (forward) for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libbsvf.so``: every step of the computation runs
+in the library (host C++ for the integer block lists, HIP kernels for norms
+and attention).  PyTorch is used only for device memory and the current
+stream.  The library must be built first (``python -m
+block_sparse_video_frame_amd.build``); without it every call raises.
+
+    blocks = build_blocks(num_frames=13, tokens_per_frame=3600, win_before=1,
+                          win_after=1, global_frames=(0,), block_q=256)
+    dev = blocks.to_device(torch.device("cuda"), batch=1, heads=8)
+    qn, kg, hm = norms(q, k)
+    o, lse = attention(q, k, v, dev, mode=SOFTMAX_BOUND, norms=(qn, kg, hm))
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "PATH_ONLINE", "PATH_BOUND",
+    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "AttnError", "lib", "library_path", "abi_version",
+    "Blocks", "DeviceBlocks", "build_blocks", "build_schedule", "norms", "attention",
+]
+
+SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED = 0, 1, 2
+PATH_ONLINE, PATH_BOUND = 0, 1
+MAX_BLOCK_Q = 256
+ELIGIBLE_NATS = 60.0
+ABI_VERSION = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libbsvf.so")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class _Pattern(ctypes.Structure):
+    _fields_ = [
+        ("num_frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
+        ("win_before", ctypes.c_int32), ("win_after", ctypes.c_int32),
+        ("num_global", ctypes.c_int32), ("global_frames", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class _Blocks(ctypes.Structure):
+    _fields_ = [
+        ("q_tiles", ctypes.c_void_p), ("kv_ptr", ctypes.c_void_p), ("kv_iv", ctypes.c_void_p),
+        ("n_qt", ctypes.c_int32), ("nnz", ctypes.c_int32), ("block_q", ctypes.c_int32),
+        ("work_order", ctypes.c_void_p), ("n_work", ctypes.c_int32),
+    ]
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_VP = ctypes.c_void_p
+
+
+def lib():
+    """Loads ``libbsvf.so`` (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m block_sparse_video_frame_amd.build`")
+    L = ctypes.CDLL(path)
+    L.attn_abi_version.restype = ctypes.c_int
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_status_str.argtypes = [ctypes.c_int]
+    L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_build_blocks.restype = ctypes.c_int
+    L.attn_build_blocks.argtypes = [ctypes.POINTER(_Pattern), ctypes.c_int32, _I32P, _I32P, _I32P,
+                                    _I64P, _I32P, _I32P]
+    L.attn_build_schedule.restype = ctypes.c_int
+    L.attn_build_schedule.argtypes = [_I32P, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P]
+    L.attn_norms.restype = ctypes.c_int
+    L.attn_norms.argtypes = [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                             _I64P, _I64P, _VP, _VP, _VP, _VP]
+    L.attn_fwd.restype = ctypes.c_int
+    L.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
+                           ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.c_float,
+                           ctypes.POINTER(_Blocks), _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    if L.attn_abi_version() != ABI_VERSION:
+        raise RuntimeError("libbsvf.so ABI version mismatch; rebuild it")
+    _LIB = L
+    return L
+
+
+def abi_version() -> int:
+    return lib().attn_abi_version()
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise AttnError(status, L.attn_last_error().decode() or L.attn_status_str(status).decode())
+
+
+def _i32(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+@dataclass
+class Blocks:
+    """Host block list (canonical form) of one pattern and tile size."""
+    q_tiles: np.ndarray   # [n_qt, 2] int32 (first token, rows)
+    kv_ptr: np.ndarray    # [n_qt + 1] int32
+    kv_iv: np.ndarray     # [nnz, 2] int32 (first key, length)
+    useful_pairs: int     # unmasked (query, key) pairs of one head
+    block_q: int
+    seq_len: int
+
+    @property
+    def n_qt(self) -> int:
+        return int(self.q_tiles.shape[0])
+
+    @property
+    def nnz(self) -> int:
+        return int(self.kv_iv.shape[0])
+
+    def to_device(self, device, batch: int, heads: int, schedule: bool = True, group: int = 32,
+                  num_xcd: int = 8) -> "DeviceBlocks":
+        import torch
+        order = build_schedule(self, batch, heads, group, num_xcd) if schedule else None
+
+        def up(x):
+            return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+        return DeviceBlocks(self, up(self.q_tiles), up(self.kv_ptr), up(self.kv_iv),
+                            up(order) if order is not None else None, batch, heads)
+
+
+@dataclass
+class DeviceBlocks:
+    host: Blocks
+    q_tiles: object
+    kv_ptr: object
+    kv_iv: object
+    work_order: object
+    batch: int
+    heads: int
+
+    def c_struct(self) -> _Blocks:
+        return _Blocks(self.q_tiles.data_ptr(), self.kv_ptr.data_ptr(), self.kv_iv.data_ptr(),
+                       self.host.n_qt, self.host.nnz, self.host.block_q,
+                       self.work_order.data_ptr() if self.work_order is not None else None,
+                       int(self.work_order.numel()) if self.work_order is not None else 0)
+
+
+def build_blocks(num_frames: int, tokens_per_frame: int, win_before: int, win_after: int,
+                 global_frames=(), block_q: int = MAX_BLOCK_Q) -> Blocks:
+    """Block list of a frame-window pattern (``attn_build_blocks``)."""
+    L = lib()
+    g = np.ascontiguousarray(np.asarray(global_frames, dtype=np.int32).reshape(-1))
+    p = _Pattern(num_frames, tokens_per_frame, win_before, win_after, len(g),
+                 _i32(g) if len(g) else None)
+    n_qt = ctypes.c_int32(0)
+    nnz = ctypes.c_int32(0)
+    useful = ctypes.c_int64(0)
+    _check(L.attn_build_blocks(ctypes.byref(p), block_q, None, None, None, ctypes.byref(useful),
+                               ctypes.byref(n_qt), ctypes.byref(nnz)))
+    qt = np.zeros((n_qt.value, 2), np.int32)
+    kp = np.zeros(n_qt.value + 1, np.int32)
+    kv = np.zeros((nnz.value, 2), np.int32)
+    _check(L.attn_build_blocks(ctypes.byref(p), block_q, _i32(qt), _i32(kp), _i32(kv),
+                               ctypes.byref(useful), ctypes.byref(n_qt), ctypes.byref(nnz)))
+    return Blocks(qt, kp, kv, int(useful.value), block_q, num_frames * tokens_per_frame)
+
+
+def build_blocks_for(pattern, block_q: int = MAX_BLOCK_Q) -> Blocks:
+    """``build_blocks`` from any object with the pattern's five attributes."""
+    return build_blocks(pattern.num_frames, pattern.tokens_per_frame, pattern.win_before,
+                        pattern.win_after, tuple(pattern.global_frames), block_q)
+
+
+def build_schedule(blocks: Blocks, batch: int, heads: int, group: int = 32, num_xcd: int = 8) -> np.ndarray:
+    """Launch order of the attention workgroups (``attn_build_schedule``)."""
+    L = lib()
+    n = ctypes.c_int32(0)
+    _check(L.attn_build_schedule(_i32(blocks.q_tiles), _i32(blocks.kv_ptr), _i32(blocks.kv_iv),
+                                 blocks.n_qt, batch, heads, group, num_xcd, None, ctypes.byref(n)))
+    out = np.zeros(n.value, np.int32)
+    _check(L.attn_build_schedule(_i32(blocks.q_tiles), _i32(blocks.kv_ptr), _i32(blocks.kv_iv),
+                                 blocks.n_qt, batch, heads, group, num_xcd, _i32(out), ctypes.byref(n)))
+    return out
+
+
+def _strides(t):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, N, D] tensor with unit stride in D")
+    return [int(t.stride(0)), int(t.stride(1)), int(t.stride(2))]
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_qkv(*ts):
+    import torch
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise ValueError("q, k, v must be bfloat16 CUDA (HIP) tensors")
+
+
+def _norms(q, k, out=None):
+    """``(q_norm [B,H,N], k_gmax [B,H,N/16], head_max [B,H,2])`` fp32 (``attn_norms``)."""
+    import torch
+    _check_qkv(q, k)
+    B, H, N, D = q.shape
+    if out is None:
+        out = (torch.empty(B, H, N, dtype=torch.float32, device=q.device),
+               torch.empty(B, H, N // 16, dtype=torch.float32, device=q.device),
+               torch.empty(B, H, 2, dtype=torch.float32, device=q.device))
+    qs = (ctypes.c_int64 * 3)(*_strides(q))
+    ks = (ctypes.c_int64 * 3)(*_strides(k))
+    _check(lib().attn_norms(q.data_ptr(), k.data_ptr(), B, H, N, D, qs, ks, out[0].data_ptr(),
+                            out[1].data_ptr(), out[2].data_ptr(), _stream(q)))
+    return out
+
+
+norms = _norms
+
+
+def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: int = SOFTMAX_BOUND,
+              norms=None, out=None, lse=None, shift_out=None, head_path=None):
+    """Block-sparse attention forward (``attn_fwd``); returns ``(out, lse)``.
+
+    ``norms``: the ``(q_norm, k_gmax, head_max)`` triple from :func:`norms`
+    (computed here when the mode needs it and none is given).
+    """
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nm = norms
+    if mode != SOFTMAX_ONLINE and nm is None:
+        nm = _norms(q, k)
+    if out is None:
+        out = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
+    st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
+    cb = blocks.c_struct()
+    qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
+    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          shift_out.data_ptr() if shift_out is not None else None,
+                          B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb), qn, kg, hm, mode,
+                          head_path.data_ptr() if head_path is not None else None, _stream(q)))
+    return out, lse

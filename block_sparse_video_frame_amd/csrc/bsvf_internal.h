@@ -1,0 +1,26 @@
+// Internal helpers shared by the host code and the kernel launchers of the
+// bsvf library.  Not part of the C ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "bsvf.h"
+
+namespace bsvf {
+
+// Records a message for attn_last_error() and returns `status`.
+int fail(int status, const std::string& msg);
+// Clears the per-thread message and returns ATTN_OK.
+int ok();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks one bf16 [B][H][N][D] tensor description: non-NULL, 16-byte aligned
+// base, strides positive multiples of 8 elements (16 bytes), rows of D
+// elements do not overlap within a head, and a head's span fits in int32
+// element offsets from the head base.
+int check_tensor(const char* name, const void* p, const int64_t* s,
+                 int32_t B, int32_t H, int32_t N, int32_t D);
+
+}  // namespace bsvf

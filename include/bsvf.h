@@ -1,0 +1,216 @@
+/*
+ * bsvf.h — C ABI of the frame-aligned block-sparse video attention library
+ * (forward pass), built for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources are web pages describing HeyGen's Avatar IV port to
+ * TPUs; cited by page and section):
+ *   - vatt-ghern.pages.dev "deep-heygen-avatar-iv-trillium-tpu", section
+ *     把 block 縮到 16: block-sparse attention whose blocks are multiples of
+ *     16 tokens and whose edges sit on frame edges, so no block is partly
+ *     masked and no padding or mask predicate is needed.  Same point in
+ *     bytechap.com "Optimizing HeyGen's Avatar IV diffusion model for Google
+ *     Cloud TPUs", section How it works, and cloudcurated.com "How is HeyGen
+ *     optimizing AI video on Google Cloud TPUs", Wall 2.
+ *   - vatt-ghern, section 拿掉 softmax 的序列相依 (also cloudcurated Wall 3):
+ *     the softmax shift of each query row may be fixed before the key loop to
+ *     the Cauchy-Schwarz bound scale*|q_i|*max|k_j| computed from precomputed
+ *     norms, which removes the running max and its rescaling; heads for which
+ *     the bound is too loose fall back to the online running max inside the
+ *     same kernel.
+ *
+ * Tokens are laid out frame by frame: token n belongs to frame n / T.  Query
+ * frame f attends key frame g when -win_before <= g - f <= win_after, or when g
+ * is one of the global frames (key side only).  Attention is bidirectional.
+ *
+ * Conventions for every function:
+ *   - Return ATTN_OK (0) or a positive ATTN_E_* status.  On error nothing has
+ *     been written and nothing launched; attn_last_error() gives a message
+ *     (per calling thread).
+ *   - Every buffer is owned by the caller.  The library allocates no memory
+ *     and keeps no state between calls; it never synchronizes.  Device work is
+ *     enqueued on the caller's stream and the call returns at once.  A device
+ *     fault surfaces at the caller's next synchronization.
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary CPU memory.
+ *   - bf16 tensors are passed as const void* to raw 16-bit bf16 storage.
+ *   - The functions are thread-safe (no shared mutable state).
+ */
+#ifndef BSVF_H
+#define BSVF_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSVF_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVAL = 1,       /* NULL pointer, non-positive size, bad enum value */
+  ATTN_E_ALIGN = 2,       /* not a multiple of 16 tokens, N != F*T, misaligned
+                             pointer or stride, d-stride != 1 */
+  ATTN_E_PATTERN = 3,     /* malformed frame pattern */
+  ATTN_E_SIZE = 4,        /* output capacity too small; sizes overflow */
+  ATTN_E_UNSUPPORTED = 5, /* head_dim not 64 or 128; block_q above the kernel's
+                             tile; bound mode without norms */
+  ATTN_E_HIP = 6          /* a HIP runtime call failed */
+};
+
+/* Softmax modes of attn_fwd. */
+enum {
+  ATTN_SOFTMAX_ONLINE = 0,       /* running max with rescaling, every head */
+  ATTN_SOFTMAX_BOUND = 1,        /* Cauchy-Schwarz shift on eligible heads,
+                                    online fallback on the rest (the method) */
+  ATTN_SOFTMAX_BOUND_FORCED = 2  /* bound on every head (diagnostic only: may
+                                    underflow to l = 0 on loose heads) */
+};
+
+/* Values written to head_path_out. */
+enum { ATTN_PATH_ONLINE = 0, ATTN_PATH_BOUND = 1 };
+
+/* Largest query tile attn_fwd accepts (its workgroup tile). */
+#define ATTN_MAX_BLOCK_Q 256
+
+/* Per-head eligibility limit in nats: a head takes the bound path in mode 1
+ * iff 2 * scale * max_n|q_n| * max_n|k_n| <= ATTN_ELIGIBLE_NATS (inclusive).
+ * This caps the gap between the fixed shift and the true row max, so the
+ * largest term exp(s - m) stays far above the float32/bf16 normal range. */
+#define ATTN_ELIGIBLE_NATS 60.0f
+
+/* Frame-window pattern (host struct). */
+typedef struct attn_pattern_t {
+  int32_t num_frames;        /* F >= 1 */
+  int32_t tokens_per_frame;  /* T: positive multiple of 16 */
+  int32_t win_before;        /* >= 0: frames attended before the query frame */
+  int32_t win_after;         /* >= 0: frames attended after the query frame */
+  int32_t num_global;        /* >= 0 */
+  const int32_t* global_frames; /* host [num_global], each in [0, F); may repeat */
+} attn_pattern_t;
+
+int attn_abi_version(void);                 /* BSVF_ABI_VERSION */
+const char* attn_status_str(int status);    /* static string, never NULL */
+const char* attn_last_error(void);          /* last failure on this thread */
+
+/*
+ * attn_build_blocks — host, integer only, deterministic.
+ * The block list of a pattern at query tile size block_q, canonical form:
+ *   q_tiles [n_qt][2] = (first token, rows).  Frame-major; frame f is cut
+ *       into T / block_q tiles of block_q rows from token f*T, then one tail
+ *       tile of T % block_q rows if that is non-zero.  No tile crosses a frame.
+ *   kv_ptr  [n_qt + 1] = CSR offsets of each tile's intervals in kv_iv.
+ *   kv_iv   [nnz][2]  = (first key token, length): the tile's attended keys as
+ *       maximal runs, ascending.  All starts and lengths are multiples of 16.
+ *   *useful_pairs = number of unmasked (query, key) pairs of one head.
+ * Two-call protocol: with q_tiles, kv_ptr and kv_iv all NULL, only *n_qt and
+ * *nnz (and *useful_pairs if non-NULL) are written.  Otherwise all three must be
+ * given and *n_qt / *nnz are read as their capacities (kv_ptr needs *n_qt + 1);
+ * ATTN_E_SIZE if too small, with the needed counts written back.
+ * Errors: ATTN_E_INVAL (NULL p, n_qt or nnz), ATTN_E_ALIGN (T or block_q not a
+ * positive multiple of 16), ATTN_E_PATTERN (F < 1, negative window, global
+ * frame out of range), ATTN_E_SIZE (F*T above INT32_MAX or capacity short).
+ */
+int attn_build_blocks(const attn_pattern_t* p, int32_t block_q,
+                      int32_t* q_tiles, int32_t* kv_ptr, int32_t* kv_iv,
+                      int64_t* useful_pairs, int32_t* n_qt, int32_t* nnz);
+
+/*
+ * attn_build_schedule — host, integer only, deterministic.
+ * Launch order for attn_fwd over batch*heads*n_qt work items (item
+ * w = tile + n_qt * (head + heads * batch_index)).  Items are ordered by
+ * decreasing cost rows*keys (ties keep the natural order, so tiles sharing
+ * their keys stay adjacent), cut into groups of `group` consecutive items, and
+ * group j is placed in the slots of workgroups that the hardware sends to
+ * accelerator die j % num_xcd (workgroup i runs on die i % num_xcd).  Unused
+ * slots hold -1 (that workgroup exits at once).  The result is a permutation of
+ * all items plus padding; it changes only the execution order, never results.
+ * Inputs are the host block list from attn_build_blocks.  Two-call protocol:
+ * with work_order NULL only *n_work is written; otherwise *n_work is the
+ * capacity (ATTN_E_SIZE if short, needed count written back).
+ * Errors: ATTN_E_INVAL (NULL arrays, non-positive sizes, group < 1,
+ * num_xcd < 1), ATTN_E_SIZE.
+ */
+int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr,
+                        const int32_t* kv_iv, int32_t n_qt, int32_t batch,
+                        int32_t heads, int32_t group, int32_t num_xcd,
+                        int32_t* work_order, int32_t* n_work);
+
+/*
+ * attn_norms — device, fp32 results, HBM-bound (reads Q and K once).
+ * The precomputed norms the bound softmax needs (vatt-ghern, section
+ * 拿掉 softmax 的序列相依):
+ *   q_norm  [B][H][N]     |q_n|_2
+ *   k_gmax  [B][H][N/16]  max |k_n|_2 over each 16-key granule
+ *   head_max[B][H][2]     (max_n |q_n|_2, max_n |k_n|_2)
+ * Outputs are contiguous fp32 device buffers.  Sums of squares accumulate in
+ * fp32.  q, k: device bf16 [B][H][N][D] addressed through element strides
+ * {b, h, n} (d-stride 1); the default contiguous layout is
+ * {H*N*D, N*D, D}, and [B][N][H][D] is {N*H*D, D, H*D}.
+ * Errors: ATTN_E_INVAL (NULL, non-positive sizes), ATTN_E_ALIGN (N % 16,
+ * pointer not 16-byte aligned, stride not a multiple of 8), ATTN_E_UNSUPPORTED
+ * (D not 64 or 128), ATTN_E_HIP (launch failed).
+ */
+int attn_norms(const void* q, const void* k, int32_t batch, int32_t heads,
+               int32_t seq_len, int32_t head_dim, const int64_t* q_strides,
+               const int64_t* k_strides, float* q_norm, float* k_gmax,
+               float* head_max, hipStream_t stream);
+
+/* Device block list for attn_fwd (pointers to device copies of the host
+ * arrays from attn_build_blocks / attn_build_schedule). */
+typedef struct attn_blocks_t {
+  const int32_t* q_tiles;    /* device [n_qt][2] */
+  const int32_t* kv_ptr;     /* device [n_qt + 1] */
+  const int32_t* kv_iv;      /* device [nnz][2] */
+  int32_t n_qt;
+  int32_t nnz;
+  int32_t block_q;           /* tile size the list was built with, <= ATTN_MAX_BLOCK_Q */
+  const int32_t* work_order; /* device [n_work] from attn_build_schedule, or NULL
+                                for the natural order (one workgroup per item) */
+  int32_t n_work;
+} attn_blocks_t;
+
+/*
+ * attn_fwd — device: the block-sparse attention forward pass.
+ *   O[b,h,i,:] = sum_j P_ij v_j,  P_ij = exp(s_ij - m_i) / l_i over the keys j
+ *   the tile of row i attends, s_ij = scale * <q_i, k_j>,
+ *   LSE[b,h,i] = m_i + ln l_i  (natural log).
+ * bf16 MFMA products with fp32 accumulation; P is rounded to bf16 for the
+ * P*V product; O is rounded to bf16 (nearest even); LSE is fp32.
+ *   q, k, v: device bf16 [B][H][N][D] via strides; o: device bf16 output.
+ *   strides: host int64 [4][3], element strides {b, h, n} of q, k, v, o
+ *       (d-stride 1 for all four).
+ *   lse: device fp32 [B][H][N] contiguous, or NULL.
+ *   shift_out: device fp32 [B][H][N] or NULL; receives the shift m_i used by
+ *       the row (natural-log units; the bound itself on bound heads).
+ *   scale: softmax scale (usually 1/sqrt(D)); must be > 0 and finite.
+ *   blocks: block list (see attn_blocks_t).  It must come from
+ *       attn_build_blocks for this N; the kernel skips any tile or interval
+ *       that lies outside [0, N) or exceeds block_q, so a corrupt list cannot
+ *       make it read or write out of bounds, but rows it skips are not written.
+ *   q_norm, k_gmax, head_max: attn_norms outputs; needed when softmax_mode is
+ *       not ATTN_SOFTMAX_ONLINE, ignored (may be NULL) otherwise.
+ *   softmax_mode: ATTN_SOFTMAX_*.  The bound shift is
+ *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-12);
+ *       the factor keeps it above every fp32-computed score.
+ *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head.
+ * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,
+ * bad mode, bad scale), ATTN_E_ALIGN (N % 16, block_q % 16, misaligned pointer
+ * or stride), ATTN_E_UNSUPPORTED (D not 64/128, block_q > ATTN_MAX_BLOCK_Q,
+ * bound mode with NULL norms), ATTN_E_SIZE (a head's span exceeds 2^31
+ * elements), ATTN_E_HIP (launch failed).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+             int32_t head_dim, const int64_t* strides, float scale,
+             const attn_blocks_t* blocks, const float* q_norm,
+             const float* k_gmax, const float* head_max, int32_t softmax_mode,
+             int32_t* head_path_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSVF_H */

@@ -1,0 +1,206 @@
+"""C-ABI library on the CPU: exported symbols, the host integer builders
+(bit-exact against the oracle's derivation from the dense mask), the launch
+schedule, and argument validation (errors are returned before any launch).
+"""
+import ctypes
+import random
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_video_frame_amd as bs
+from oracle import blocks as BL
+from synth import WORKLOADS, Pattern
+
+HEADER = __import__("os").path.join(__import__("os").path.dirname(__file__), "..", "include", "bsvf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"attn_build_blocks", "attn_build_schedule", "attn_norms", "attn_fwd",
+            "attn_abi_version", "attn_status_str", "attn_last_error"} <= set(names)
+    L = ctypes.CDLL(bs.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    assert bs.abi_version() == 1
+    assert bs.lib().attn_status_str(3) == b"ATTN_E_PATTERN"
+
+
+def as_lists(blk):
+    return ([tuple(x) for x in blk.q_tiles.tolist()], blk.kv_ptr.tolist(),
+            [tuple(x) for x in blk.kv_iv.tolist()])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("bq", [16, 128, 256])
+def test_builder_matches_oracle_on_workloads(name, bq):
+    p = WORKLOADS[name].pattern
+    got = bs.build_blocks_for(p, bq)
+    want = BL.derive_blocks(p, bq)
+    qt, kp, kv = as_lists(got)
+    assert qt == want["q_tiles"] and kp == want["kv_ptr"] and kv == want["kv_iv"]
+    assert got.useful_pairs == want["useful_pairs"]
+
+
+def test_builder_matches_oracle_on_random_patterns():
+    rnd = random.Random(11)
+    for _ in range(150):
+        F = rnd.randint(1, 20)
+        T = 16 * rnd.randint(1, 32)
+        gl = tuple(sorted(set(rnd.randint(0, F - 1) for _ in range(rnd.randint(0, 3)))))
+        p = Pattern(F, T, rnd.randint(0, 3), rnd.randint(0, 3), gl)
+        bq = 16 * rnd.randint(1, 32)
+        got = bs.build_blocks_for(p, bq)
+        want = BL.derive_blocks(p, bq, check_rows="all" if F * T <= 2048 else "ends")
+        qt, kp, kv = as_lists(got)
+        assert qt == want["q_tiles"] and kp == want["kv_ptr"] and kv == want["kv_iv"], p
+        assert got.useful_pairs == want["useful_pairs"]
+
+
+def test_builder_repeated_global_frames_are_merged():
+    a = bs.build_blocks(6, 32, 0, 0, (2, 2, 4), 32)
+    b = bs.build_blocks(6, 32, 0, 0, (4, 2), 32)
+    assert as_lists(a) == as_lists(b)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 40, 1, 1, (), 32), 2),        # T not a multiple of 16
+    ((4, 48, 1, 1, (), 24), 2),        # block_q not a multiple of 16
+    ((4, 48, 1, 1, (), 0), 2),
+    ((0, 48, 1, 1, (), 32), 3),        # no frames
+    ((4, 48, -1, 1, (), 32), 3),       # negative window
+    ((4, 48, 1, 1, (4,), 32), 3),      # global frame out of range
+    ((1 << 20, 4096, 1, 1, (), 256), 4),  # F*T above INT32_MAX
+])
+def test_builder_errors(args, status):
+    with pytest.raises(bs.AttnError) as e:
+        bs.build_blocks(*args)
+    assert e.value.status == status
+
+
+def test_builder_capacity_protocol():
+    L = bs.lib()
+    p = bs._Pattern(5, 64, 1, 1, 0, None)
+    n_qt, nnz = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert L.attn_build_blocks(ctypes.byref(p), 32, None, None, None, None, ctypes.byref(n_qt), ctypes.byref(nnz)) == 0
+    assert (n_qt.value, nnz.value) == (10, 10)
+    qt = np.zeros((9, 2), np.int32); kp = np.zeros(10, np.int32); kv = np.zeros((10, 2), np.int32)
+    small = ctypes.c_int32(9)
+    st = L.attn_build_blocks(ctypes.byref(p), 32, bs._i32(qt), bs._i32(kp), bs._i32(kv), None,
+                             ctypes.byref(small), ctypes.byref(nnz))
+    assert st == 4 and small.value == 10
+    assert b"capacity" in L.attn_last_error()
+    assert not qt.any() and not kp.any()
+    # NULL pattern / counts
+    assert L.attn_build_blocks(None, 32, None, None, None, None, ctypes.byref(n_qt), ctypes.byref(nnz)) == 1
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_schedule_is_a_padded_permutation(name):
+    wl = WORKLOADS[name]
+    blk = bs.build_blocks_for(wl.pattern, 256)
+    items = blk.n_qt * wl.heads * wl.batch
+    for group, xcd in [(32, 8), (15, 8), (1, 1), (7, 3)]:
+        order = bs.build_schedule(blk, wl.batch, wl.heads, group, xcd)
+        assert len(order) % (group * xcd) == 0 and len(order) >= items
+        real = order[order >= 0]
+        assert sorted(real.tolist()) == list(range(items))
+        assert (order[order < 0] == -1).all()
+        # every die's queue runs longest work first
+        cost = {}
+        for t in range(blk.n_qt):
+            keys = blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum()
+            cost[t] = int(keys) * int(blk.q_tiles[t, 1])
+        for x in range(xcd):
+            seq = [cost[w % blk.n_qt] for w in order[x::xcd] if w >= 0]
+            assert all(a >= b for a, b in zip(seq, seq[1:]))
+    o1 = bs.build_schedule(blk, wl.batch, wl.heads)
+    o2 = bs.build_schedule(blk, wl.batch, wl.heads)
+    assert (o1 == o2).all()
+
+
+def test_schedule_errors():
+    blk = bs.build_blocks(3, 32, 1, 1, (), 32)
+    with pytest.raises(bs.AttnError):
+        bs.build_schedule(blk, 1, 1, 0, 8)
+    with pytest.raises(bs.AttnError):
+        bs.build_schedule(blk, 0, 1, 4, 8)
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# The validation cases below pass addresses that are never dereferenced: each
+# case carries an argument that the library rejects before any HIP call.  They
+# run where no GPU is visible only.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="validation-only test for CPU hosts")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def fwd_call(**over):
+    L = bs.lib()
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, shift=None, B=1, H=2, N=192, D=64,
+                strides=[192 * 64 * 2, 192 * 64, 64] * 4, scale=0.125, blocks="ok",
+                qn=None, kg=None, hm=None, mode=0, hp=None)
+    args.update(over)
+    st = (ctypes.c_int64 * 12)(*args["strides"]) if args["strides"] is not None else None
+    cb = bs._Blocks(FAKE, FAKE, FAKE, 4, 4, 256, None, 0)
+    if isinstance(args["blocks"], dict):
+        for k, v in args["blocks"].items():
+            setattr(cb, k, v)
+    bp = ctypes.byref(cb) if args["blocks"] is not None else None
+    return L.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["shift"],
+                      args["B"], args["H"], args["N"], args["D"], st, ctypes.c_float(args["scale"]), bp,
+                      args["qn"], args["kg"], args["hm"], args["mode"], args["hp"], None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1),
+    (dict(blocks=None), 1),
+    (dict(strides=None), 1),
+    (dict(B=0), 1),
+    (dict(mode=3), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(D=96), 5),
+    (dict(N=200), 2),
+    (dict(q=FAKE + 2), 2),
+    (dict(strides=[192 * 64 * 2, 192 * 64, 60] + [192 * 64 * 2, 192 * 64, 64] * 3), 2),
+    (dict(strides=[192 * 64 * 2, 192 * 64, 32] + [192 * 64 * 2, 192 * 64, 64] * 3), 2),
+    (dict(blocks={"block_q": 24}), 2),
+    (dict(blocks={"block_q": 512}), 5),
+    (dict(blocks={"n_qt": 0}), 1),
+    (dict(blocks={"q_tiles": None}), 1),
+    (dict(mode=1), 5),                 # bound mode without norms
+    (dict(N=1 << 26, strides=[(1 << 26) * 64 * 2, (1 << 26) * 64, 64] * 4), 4),  # head span > 2^31
+])
+def test_fwd_validation(over, status):
+    assert fwd_call(**over) == status
+    assert bs.lib().attn_last_error().startswith(bs.lib().attn_status_str(status))
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), 1), (dict(D=32), 5), (dict(N=100), 2), (dict(k=FAKE + 8), 2), (dict(qn=None), 1),
+])
+def test_norms_validation(over, status):
+    L = bs.lib()
+    a = dict(q=FAKE, k=FAKE, B=1, H=2, N=192, D=64, qn=FAKE, kg=FAKE, hm=FAKE)
+    a.update(over)
+    s = (ctypes.c_int64 * 3)(a["N"] * a["D"] * 2, a["N"] * a["D"], a["D"])
+    st = L.attn_norms(a["q"], a["k"], a["B"], a["H"], a["N"], a["D"], s, s, a["qn"], a["kg"], a["hm"], None)
+    assert st == status
