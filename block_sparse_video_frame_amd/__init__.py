@@ -38,7 +38,8 @@ _LIB = None
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libbsvf.so")
+    """The in-tree build, or the file named by ``BSVF_LIBRARY``."""
+    return os.environ.get("BSVF_LIBRARY") or os.path.join(_HERE, "libbsvf.so")
 
 
 class AttnError(RuntimeError):

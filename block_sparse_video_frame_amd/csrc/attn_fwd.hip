@@ -44,11 +44,16 @@ constexpr int BK = 64;  // keys per LDS stage
 #define BOUND_NQB 1
 #define BOUND_NW 8
 #endif
+// s_waitcnt immediate that waits for every outstanding vector memory access
+// (vmcnt 0) and leaves the export and LDS counters alone.
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Keeps the fp32 bound above every fp32-computed score: the dot-product and
-// norm rounding errors are below D * 2^-24 relative for D <= 128.
-constexpr float kBoundMargin = 1.0f + 1.0f / 4096.0f;
+// The bound path keeps Q pre-multiplied by scale*log2(e) and rounded to bf16
+// (each element off by at most 2^-9 relative), so its scores can exceed
+// scale*log2(e)*|q|*|k| by that much; the margin covers it with room for the
+// fp32 dot-product and norm rounding (below D * 2^-24 for D <= 128).
+constexpr float kBoundMargin = 1.0f + 1.0f / 256.0f;
 
 struct FwdArgs {
   const u16* q;
@@ -87,6 +92,13 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
   return r;
 }
 
+// p0 + p1 + acc for a packed bf16 pair (one v_dot2 with (1, 1)): the row sum
+// adds exactly the rounded probabilities the P*V product uses.
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
 __device__ __forceinline__ bool interval_ok(int ks, int kl, int N) {
   return ks >= 0 && kl > 0 && ((ks | kl) & 15) == 0 && ks <= N - kl;
 }
@@ -95,117 +107,196 @@ template <int D, int NQB, int NW>
 struct Cfg {
   static constexpr int NT = 64 * NW;
   static constexpr int BQ = 32 * NQB * NW;
-  static constexpr int DC = D / 8;               // 16-byte chunks per K row
+  static constexpr int DC = D / 8;               // 16-byte chunks per K/V row
   static constexpr int KSTEPS = D / 16;          // MFMA k-steps of Q*K^T
   static constexpr int DBLK = D / 32;            // 32-wide output blocks
-  static constexpr int STAGE = 2 * BK * D;       // K + V^T elements per stage
-  static constexpr int K_LOADS = BK * DC / NT;   // 16-byte K loads per thread
-  static constexpr int KPT = BK * D / (NT * 8);  // V keys per thread
-  static_assert(K_LOADS >= 1 && KPT >= 1 && KPT <= 4 && (4 % KPT) == 0, "tile shape");
+  static constexpr int REGION = BK * D;          // elements of K (or V) per stage
+  static constexpr int STAGE = 2 * REGION;       // K + V elements per stage
+  static constexpr int LPW = DC / NW;            // 1 KiB direct loads per wave per region
+  static_assert(LPW >= 1 && LPW * NW == DC, "tile shape");
 };
 
-// Global -> registers -> LDS staging of one 64-key stage.  Keys past the
-// stage's valid count re-load the last valid key (always in bounds and finite);
-// their probabilities are zeroed before they can contribute.
+// LDS layout of a stage: K rows then V rows, [64 keys][D] bf16 each, with the
+// 16-byte chunk c of row r stored at chunk position c ^ swz(r).  LDS has 64
+// four-byte banks; a 16-byte read is served 16 lanes at a time and an 8-byte
+// (transposing) read 32 lanes at a time.  The swizzle spreads both the K
+// operand reads (16 consecutive rows, one chunk) and the transposing V reads
+// (4 consecutive rows x 4 adjacent chunks per 32 lanes) over all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int col) {
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor over one head's rows of K or V (raw buffer, byte
+// offsets).  Reads at offsets past `bytes` return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const u16* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-lane byte offsets of the LDS-DMA loads of a stage that is one
+// contiguous run of 64 keys: key row `row` of the run at the chunk the swizzle
+// puts at this lane's LDS slot.  The run's start enters as a scalar offset.
 template <int D, int NQB, int NW>
-struct Stager {
+struct DmaLanes {
+  uint32_t k[Cfg<D, NQB, NW>::LPW];
+  uint32_t v[Cfg<D, NQB, NW>::LPW];
+  __device__ __forceinline__ void init(uint32_t ksn, uint32_t vsn, int wave, int lane) {
+    using C = Cfg<D, NQB, NW>;
+#pragma unroll
+    for (int it = 0; it < C::LPW; ++it) {
+      const int slot = (it * NW + wave) * 64 + lane;
+      const int row = slot / C::DC, phys = slot % C::DC;
+      const uint32_t col = (phys ^ swz<D>(row)) << 3;
+      k[it] = 2u * (row * ksn + col);
+      v[it] = 2u * (row * vsn + col);
+    }
+  }
+};
+
+// Direct global -> LDS copy of one stage that is a contiguous run of keys
+// start .. start+63.  Each wave-wide load fills 1 KiB of LDS in lane order, so
+// every lane fetches the chunk the swizzle places at its LDS slot.
+template <int D, int NQB, int NW>
+__device__ __forceinline__ void issue_stage_run(u16* ks, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                            const DmaLanes<D, NQB, NW>& dl, uint32_t ksn, uint32_t vsn,
+                                            int start, int wave) {
   using C = Cfg<D, NQB, NW>;
-  u32x4 kr[C::K_LOADS];
-  u32x4 vr[C::KPT];
-
-  __device__ __forceinline__ void load(const u16* kh, const u16* vh, int ksn, int vsn,
-                                       int start, int nvalid, int tid) {
+  const uint32_t sk = 2u * (uint32_t)start * ksn, sv = 2u * (uint32_t)start * vsn;
 #pragma unroll
-    for (int it = 0; it < C::K_LOADS; ++it) {
-      const int idx = it * C::NT + tid;
-      const int key = min(idx / C::DC, nvalid - 1), c = idx % C::DC;
-      kr[it] = *reinterpret_cast<const u32x4*>(kh + (start + key) * ksn + 8 * c);
-    }
-    const int dg = tid % C::DC, kg = tid / C::DC;
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      const int key = min(kg * C::KPT + j, nvalid - 1);
-      vr[j] = *reinterpret_cast<const u32x4*>(vh + (start + key) * vsn + 8 * dg);
-    }
+  for (int it = 0; it < C::LPW; ++it) {
+    const int blk = it * NW + wave;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + blk * 512), 16, (int)dl.k[it], (int)sk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::REGION + blk * 512), 16, (int)dl.v[it],
+                                             (int)sv, 0, 0);
   }
+}
 
-  __device__ __forceinline__ void store(u16* ks, u16* vt, int tid) const {
-#pragma unroll
-    for (int it = 0; it < C::K_LOADS; ++it) {
-      const int idx = it * C::NT + tid;
-      const int key = idx / C::DC, c = idx % C::DC;
-      *reinterpret_cast<u32x4*>(ks + key * D + ((c ^ (key & (C::DC - 1))) << 3)) = kr[it];
-    }
-    // V^T: row d holds the stage's 64 keys.  Inside each 16-key group the
-    // 4-key subgroups sit in the order 0, 2, 1, 3, so that the 8 keys one
-    // lane half feeds to the P*V MFMA are contiguous; 16-byte chunks of a row
-    // are XOR-swizzled by (d ^ d>>3) & 7.
-    const int dg = tid % C::DC, kg = tid / C::DC;
-    const int key0 = kg * C::KPT;
-    const int s4 = (key0 >> 2) & 3;
-    const int pos = (key0 & ~15) + 4 * (((s4 & 1) << 1) | (s4 >> 1)) + (key0 & 3);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * dg + e;
-      const int off = d * BK + ((((pos >> 3) ^ (d ^ (d >> 3))) & 7) << 3) + (pos & 7);
-      uint32_t h[C::KPT];
-#pragma unroll
-      for (int j = 0; j < C::KPT; ++j) {
-        const uint32_t w = vr[j][e >> 1];
-        h[j] = (e & 1) ? (w >> 16) : (w & 0xffffu);
-      }
-      if constexpr (C::KPT == 4) {
-        u32x2 pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        *reinterpret_cast<u32x2*>(vt + off) = pk;
-      } else if constexpr (C::KPT == 2) {
-        *reinterpret_cast<uint32_t*>(vt + off) = h[0] | (h[1] << 16);
-      } else {
-        vt[off] = (u16)h[0];
-      }
-    }
-  }
+// A stage in general: the next 64 positions of the tile's keys, taken in
+// order across its intervals (at most four, as every interval holds a
+// multiple of 16 keys).  Position r < end[j] (first such j) is key base[j] + r;
+// positions at or past `n` do not exist (only the tile's last stage is short).
+struct StageDesc {
+  int base[4];
+  int end[4];
+  int n;
 };
 
+// Direct global -> LDS copy of a general stage.  Positions past the stage's
+// count re-load its last key (in bounds, finite); their probabilities are
+// zeroed before use.
 template <int D, int NQB, int NW>
+__device__ __forceinline__ void issue_stage(u16* ks, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                            uint32_t ksn, uint32_t vsn, const StageDesc& sd, int wave,
+                                            int lane) {
+  using C = Cfg<D, NQB, NW>;
+#pragma unroll
+  for (int it = 0; it < C::LPW; ++it) {
+    const int blk = it * NW + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / C::DC, phys = slot % C::DC;
+    const uint32_t col = (phys ^ swz<D>(row)) << 3;
+    const int r = min(row, sd.n - 1);
+    const int base = r < sd.end[0] ? sd.base[0] : r < sd.end[1] ? sd.base[1] : r < sd.end[2] ? sd.base[2] : sd.base[3];
+    const uint32_t key = base + r;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + blk * 512), 16, 2 * (key * ksn + col), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::REGION + blk * 512), 16,
+                                             2 * (key * vsn + col), 0, 0, 0);
+  }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// 16-byte LDS read that the compiler issues where it is written (volatile),
+// used to start operand reads several MFMAs ahead of their use.
+__device__ __forceinline__ bf16x8 lds_read_early(const u16* p) {
+  return *(const volatile lds_bf16x8*)(p);
+}
+
+// Transposing LDS read: within each 16-lane group, output lane i element j is
+// element i % 4 of the 8 bytes addressed by lane 4j + i / 4.
+__device__ __forceinline__ i16x4 ds_read_tr16(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// P*V: the transposing V reads (two per MFMA) start PV_AHEAD MFMAs before the
+// MFMA that consumes them, so LDS latency hides behind matrix work.
+#ifndef PV_AHEAD
+#define PV_AHEAD 1
+#endif
+// K operand reads start KAHEAD MFMAs before their use in the fused step.
+#ifndef KAHEAD
+#define KAHEAD 2
+#endif
+template <int NMFMA>
+__device__ __forceinline__ void pin_pv() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 1);
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+}
+
+template <int D, int NQB, int NW, bool BOUNDQ>
 struct Tile {
   using C = Cfg<D, NQB, NW>;
+  using Scores = f32x16[2][NQB];
+  using Probs = bf16x8[NQB][2][2];
   bf16x8 qreg[NQB][C::KSTEPS];
   f32x16 oacc[NQB][C::DBLK];
   float m2[NQB];    // row shift in log2 units (bound: fixed; online: running max)
   float lsum[NQB];  // this lane half's share of the row sum
-  int n, hh;
+  int n, hh, lane;
 
-  // One LDS stage: 64 keys of which the first `nvalid` (16, 32, 48 or 64) are
-  // real.  The same MFMAs run for every stage; a short stage only zeroes the
-  // probabilities of its missing keys.
-  template <bool BOUND>
-  __device__ __forceinline__ void stage(const u16* ks, const u16* vt, int nvalid, float c2) {
-    f32x16 s[2][NQB];
+  // Score accumulators start at acc0[qb]: the bound path starts at -m (its Q
+  // already carries scale*log2(e)), so the MFMA yields the exponent directly.
+  __device__ __forceinline__ float acc0(int qb) const { return BOUNDQ ? -m2[qb] : 0.0f; }
+
+  // S^T = K * Q^T for the 64 keys of a stage: lane (n, hh) gets keys
+  // 32kb + 8i + 4hh + j (register 4i + j) of query n.
+  __device__ __forceinline__ void scores(const u16* ks, Scores& s) const {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.0f;
-    // S^T = K * Q^T: lane (n, hh) gets keys 32kb + 8i + 4hh + j (register
-    // 4i + j) of query n.
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = acc0(qb);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = 32 * kb + n;
+    for (int st = 0; st < C::KSTEPS; ++st)
 #pragma unroll
-      for (int st = 0; st < C::KSTEPS; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + key * D + (((2 * st + hh) ^ (key & (C::DC - 1))) << 3));
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + lds_off<D>(32 * kb + n, 16 * st + 8 * hh));
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][st], s[kb][qb], 0, 0, 0);
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[qb][st], s[kb][qb], 0, 0, 0);
       }
-    }
-    bf16x8 pk[NQB][2][2];
+  }
+
+  // Probabilities of one stage as bf16 MFMA operands.  Bound: exp(s - m) with
+  // the fixed shift, no max and no rescale.  Online: raise the running max;
+  // alpha[qb] is the factor the accumulator still has to be rescaled by.
+  // TAIL: only the first `nvalid` keys of the stage are real (a multiple of
+  // 16, so keys 32kb + 8i .. +7 are all real or all missing).
+  template <bool BOUND, bool TAIL>
+  __device__ __forceinline__ void softmax(const Scores& s, Probs& pk, float (&alpha)[NQB], int nvalid,
+                                          float c2) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
+      alpha[qb] = 1.0f;
       if constexpr (!BOUND) {
-        // Running max over the stage (missing keys hold copies of a real key of
-        // this row, so they cannot raise the max above a real score).
+        // Missing keys hold copies of a real key of this row, so they cannot
+        // raise the max above a real score.
         float mx = s[0][qb][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -213,98 +304,314 @@ struct Tile {
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m2[qb], mx * c2);
-        const float alpha = __builtin_amdgcn_exp2f(m2[qb] - mnew);
+        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - mnew);
         m2[qb] = mnew;
-        lsum[qb] *= alpha;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < C::DBLK; ++db) oacc[qb][db] *= alpha;
-        }
+        lsum[qb] *= alpha[qb];
       }
       const float nm = -m2[qb];
       float p[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c2, nm));
-      if (nvalid < BK) {
-        // keys 32kb + 8i .. +7 are all real or all missing (16-key granules)
+        for (int r = 0; r < 16; ++r)
+          p[kb][r] = __builtin_amdgcn_exp2f(BOUND ? s[kb][qb][r] : fmaf(s[kb][qb][r], c2, nm));
+      if constexpr (TAIL) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (32 * kb + 8 * i >= nvalid)
+          for (int i = 0; i < 4; ++i) {
+            const bool live = 32 * kb + 8 * i < nvalid;
 #pragma unroll
-              for (int j = 0; j < 4; ++j) p[kb][4 * i + j] = 0.0f;
+            for (int j = 0; j < 4; ++j) p[kb][4 * i + j] = live ? p[kb][4 * i + j] : 0.0f;
+          }
       }
-      float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f, t3 = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        t0 += p[0][r]; t1 += p[0][r + 1]; t2 += p[1][r]; t3 += p[1][r + 1];
-      }
-      lsum[qb] += (t0 + t1) + (t2 + t3);
+      float t0 = 0.0f, t1 = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         pk[qb][kb][0] = to_bf16x8(p[kb]);
         pk[qb][kb][1] = to_bf16x8(p[kb] + 8);
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst) {
+          const u32x4 w = __builtin_bit_cast(u32x4, pk[qb][kb][kst]);
+          t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
+          t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+        }
       }
+      lsum[qb] += t0 + t1;
     }
-    // O^T += V^T * P^T: k-step (kb, kst) covers keys 32kb + 16kst + [0, 16).
+  }
+
+  // The softmax of a full stage (`cur`) fused with the Q*K^T MFMAs of the
+  // next stage (`nxt`, K operands from `ks`).  The two are independent, so the
+  // code is laid out as one chunk per MFMA -- a K operand read three MFMAs
+  // ahead, the MFMA, then a slice of the softmax -- and sched_barrier keeps
+  // the compiler from regrouping the chunks: the matrix core runs while the
+  // vector ALU works.  Results equal softmax<BOUND, false> then scores().
+  template <bool BOUND>
+  __device__ __forceinline__ void softmax_and_scores(const Scores& cur, const u16* ks, Scores& nxt,
+                                                     Probs& pk, float (&alpha)[NQB], float c2) {
+    constexpr int NM = 2 * C::KSTEPS;       // MFMAs per 32 queries (st, kb)
+    constexpr int EPM = 32 / NM;            // softmax elements per MFMA (2 or 4)
+    constexpr int AHEAD = KAHEAD;
+    float nm[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      alpha[qb] = 1.0f;
+      if constexpr (!BOUND) {
+        float mx = cur[0][qb][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][qb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m2[qb], mx * c2);
+        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - mnew);
+        m2[qb] = mnew;
+        lsum[qb] *= alpha[qb];
+      }
+      nm[qb] = -m2[qb];
+    }
+    // MFMA i accumulates block kbn(i) of the next stage: the first half of the
+    // chunks fills block 1 while block 0 of `cur` is being consumed, the second
+    // half fills block 0 once those registers are free (48 live score
+    // registers per 32 queries instead of 64).
+    auto kbn = [](int i) { return i < C::KSTEPS ? 1 : 0; };
+    auto stn = [](int i) { return i % C::KSTEPS; };
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nxt[1][qb][r] = acc0(qb);
+    // K operand reads are volatile so they issue AHEAD MFMAs before their use
+    // instead of being sunk next to it.
+    bf16x8 kf[NM];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i)
+      kf[i] = lds_read_early(ks + lds_off<D>(32 * kbn(i) + n, 16 * stn(i) + 8 * hh));
+    float part[NQB][2];
+    uint32_t pw[NQB][2][8];  // packed bf16 pairs: [qb][kb][r / 2]
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) part[qb][0] = part[qb][1] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + AHEAD < NM) {
+        const int j = i + AHEAD;
+        kf[j] = lds_read_early(ks + lds_off<D>(32 * kbn(j) + n, 16 * stn(j) + 8 * hh));
+      }
+      if (i == C::KSTEPS) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) nxt[0][qb][r] = acc0(qb);
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+        nxt[kbn(i)][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[qb][stn(i)], nxt[kbn(i)][qb], 0, 0, 0);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int e = 0; e < EPM; e += 2) {
+          const int el = i * EPM + e, kb = el >> 4, r = el & 15;
+          const float p0 = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r] : fmaf(cur[kb][qb][r], c2, nm[qb]));
+          const float p1 = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r + 1] : fmaf(cur[kb][qb][r + 1], c2, nm[qb]));
+          f32x2 f = {p0, p1};
+          const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+          pw[qb][kb][r >> 1] = w;
+          part[qb][(e >> 1) & 1] = add_pair(w, part[qb][(e >> 1) & 1]);
+          // keep this slice here: without a use at this point the compiler
+          // sinks the whole softmax below the MFMAs
+          asm volatile("" : "+v"(part[qb][0]), "+v"(part[qb][1]), "+v"(pw[qb][kb][r >> 1]));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      lsum[qb] += part[qb][0] + part[qb][1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kst = 0; kst < 2; ++kst) {
+          u32x4 w = {pw[qb][kb][4 * kst], pw[qb][kb][4 * kst + 1], pw[qb][kb][4 * kst + 2], pw[qb][kb][4 * kst + 3]};
+          pk[qb][kb][kst] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+  }
+
+  // Online path: apply the pending rescale to the accumulator, skipped when
+  // no row of the wave raised its max.
+  __device__ __forceinline__ void rescale(const float (&alpha)[NQB]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+      if (__any(alpha[qb] != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) oacc[qb][db] *= alpha[qb];
+      }
+  }
+
+  // O^T += V^T * P^T: k-step (kb, kst) covers keys 32kb + 16kst + [0, 16);
+  // lane (n, hh) needs V[32kb + 16kst + 8(e/4) + 4hh + e%4][32db + n] as its
+  // element e, which two transposing reads deliver: source lane t of each
+  // 16-lane group addresses key row (... + 4hh + t/4) at columns
+  // 32db + 16((lane/16)%2) + 4(t%4) .. +3.
+  __device__ __forceinline__ void pv(const u16* vs, const Probs& pk) {
+    const int t16 = lane & 15, g2 = (lane >> 4) & 1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db) {
-          const int d = 32 * db + n;
-          const int chunk = 2 * (2 * kb + kst) + hh;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + d * BK + ((chunk ^ ((d ^ (d >> 3)) & 7)) << 3));
+          const int row = 32 * kb + 16 * kst + 4 * hh + (t16 >> 2);
+          const int col = 32 * db + 16 * g2 + 4 * (t16 & 3);
+          const i16x4 lo = ds_read_tr16(vs + lds_off<D>(row, col));
+          const i16x4 hi = ds_read_tr16(vs + lds_off<D>(row + 8, col));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < NQB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][kb][kst], oacc[qb][db], 0, 0, 0);
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[qb][kb][kst], oacc[qb][db], 0, 0, 0);
         }
   }
 };
 
-template <int D, int NQB, int NW, bool BOUND>
-__device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
-                                         Tile<D, NQB, NW>& T, const u16* kh, const u16* vh,
-                                         int e0, int e1, int tid) {
-  using C = Cfg<D, NQB, NW>;
-  const int ksn = (int)a.sk[2], vsn = (int)a.sv[2];
-  // Walk the tile's intervals in stages of up to 64 keys.
-  int e = e0;
-  while (e < e1 && !interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) ++e;
-  if (e >= e1) return;
-  int cs = kv_iv[2 * e], cl = kv_iv[2 * e + 1];  // current interval
-  int off = 0;
-  Stager<D, NQB, NW> sg;
-  int cur_n = min(BK, cl);
-  sg.load(kh, vh, ksn, vsn, cs, cur_n, tid);
-  sg.store(smem, smem + BK * D, tid);
-  __syncthreads();
-  int buf = 0;
-  while (true) {
-    int noff = off + BK, ncs = cs, ncl = cl, ne = e;
-    bool has_next = true;
-    if (noff >= cl) {
-      noff = 0;
-      ++ne;
-      while (ne < e1 && !interval_ok(kv_iv[2 * ne], kv_iv[2 * ne + 1], a.N)) ++ne;
-      if (ne >= e1) has_next = false;
-      else { ncs = kv_iv[2 * ne]; ncl = kv_iv[2 * ne + 1]; }
-    }
-    const int next_n = has_next ? min(BK, ncl - noff) : 0;
-    if (has_next) sg.load(kh, vh, ksn, vsn, ncs + noff, next_n, tid);
-    u16* ks = smem + buf * C::STAGE;
-    T.template stage<BOUND>(ks, ks + BK * D, cur_n, a.c2);
-    if (!has_next) break;
-    u16* nks = smem + (buf ^ 1) * C::STAGE;
-    sg.store(nks, nks + BK * D, tid);
-    __syncthreads();
-    buf ^= 1;
-    e = ne; cs = ncs; cl = ncl; off = noff; cur_n = next_n;
+// s_waitcnt immediate that waits until at most n vector memory accesses of
+// this wave are outstanding (they complete in order), leaving the export and
+// LDS counters alone.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Stages in flight ahead of the one being consumed, and LDS buffers: the
+// prefetch window, the stage being consumed, and the lagging half's previous
+// stage (see run_tile).
+constexpr int kPrefetch = 2;
+constexpr int kBuffers = kPrefetch + 2;
+
+// Cuts the tile's valid intervals into consecutive 64-key stages (scalar,
+// uniform state).  Intervals outside [0, N) or not 16-aligned are skipped.
+struct KeyWalker {
+  const int32_t* __restrict__ kv_iv;
+  int e, e1, N, cs, cl, off;
+  bool more;
+
+  __device__ __forceinline__ void seek() {
+    while (e < e1 && !interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], N)) ++e;
+    more = e < e1;
+    if (more) { cs = kv_iv[2 * e]; cl = kv_iv[2 * e + 1]; off = 0; }
   }
+  // Next stage.  Returns true when it is one contiguous run of 64 keys (the
+  // common case), given by `start`; otherwise fills `d`.
+  __device__ __forceinline__ bool next(StageDesc& d, int& start) {
+    if (more && cl - off >= BK) {
+      start = cs + off;
+      off += BK;
+      if (off >= cl) { ++e; seek(); }
+      return true;
+    }
+    int pos = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (more && pos < BK) {
+        const int take = min(cl - off, BK - pos);
+        d.base[k] = cs + off - pos;
+        pos += take;
+        off += take;
+        if (off >= cl) { ++e; seek(); }
+      } else {
+        d.base[k] = k ? d.base[k - 1] : 0;
+      }
+      d.end[k] = pos;
+    }
+    d.n = pos;
+    return false;
+  }
+};
+
+// Software-pipelined walk over the tile's stages with kBuffers LDS buffers
+// (stage x lives in buffer x mod kBuffers).  Per iteration s, after one
+// barrier, stage s+kPrefetch starts streaming in, and each wave runs F(s) --
+// the softmax of stage s fused with the Q*K^T MFMAs of stage s+1 (VALU-heavy)
+// -- and a P*V step (MFMA only).  The two waves that share a SIMD run them in
+// opposite orders: the leading half of the workgroup does F(s) then P(s); the
+// lagging half does P(s-1) then F(s).  One wave's vector work then overlaps
+// the other's matrix work instead of both contending for the same unit.
+// Every stage but the tile's last is full.
+template <int D, int NQB, int NW, bool BOUND, bool LAG>
+__device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
+                                         Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh,
+                                         int e0, int e1, int wave) {
+  using C = Cfg<D, NQB, NW>;
+  using TT = Tile<D, NQB, NW, BOUND>;
+  constexpr int LOADS = 2 * C::LPW;  // vector memory ops per wave per stage
+  static_assert((kBuffers & (kBuffers - 1)) == 0, "buffer count must be a power of two");
+  const uint32_t ksn = (uint32_t)a.sk[2], vsn = (uint32_t)a.sv[2];
+  const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, 2u * (ksn * (uint32_t)(a.N - 1) + D));
+  const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, 2u * (vsn * (uint32_t)(a.N - 1) + D));
+  int total = 0;
+  for (int e = e0; e < e1; ++e)
+    if (interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) total += kv_iv[2 * e + 1];
+  if (total == 0) return;
+  const int ns = (total + BK - 1) / BK, nlast = total - BK * (ns - 1);
+  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::STAGE; };
+  auto vbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::STAGE + C::REGION; };
+  KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
+  kw.seek();
+  DmaLanes<D, NQB, NW> dl;
+  dl.init(ksn, vsn, wave, T.lane);
+  auto issue = [&](int x) {
+    StageDesc sd;
+    int start;
+    if (kw.next(sd, start)) issue_stage_run<D, NQB, NW>(kbuf(x), kr, vr, dl, ksn, vsn, start, wave);
+    else issue_stage<D, NQB, NW>(kbuf(x), kr, vr, ksn, vsn, sd, wave, T.lane);
+  };
+#pragma unroll
+  for (int x = 0; x < kPrefetch; ++x)
+    if (x < ns) issue(x);
+  __builtin_amdgcn_s_waitcnt(wait_vm((kPrefetch - 1) * LOADS));  // stage 0 landed, if it was not alone
+  if (ns < kPrefetch) __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  typename TT::Scores sc;
+  T.scores(kbuf(0), sc);
+  typename TT::Probs pk;
+  float alpha[NQB];
+  auto step = [&](int st, typename TT::Scores& cur, typename TT::Scores& nxt) {
+    // Stage st+1 has landed (every wave): at most the stages after it are
+    // still in flight.  Every wave is also done with the buffer stage
+    // st+kPrefetch is about to overwrite.
+    if (st + kPrefetch - 1 < ns) __builtin_amdgcn_s_waitcnt(wait_vm((kPrefetch - 2) * LOADS));
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (st + kPrefetch < ns) issue(st + kPrefetch);
+    if constexpr (LAG) {
+      if (st > 0) {
+        T.pv(vbuf(st - 1), pk);
+        pin_pv<4 * C::DBLK * NQB>();
+      }
+      T.template softmax_and_scores<BOUND>(cur, kbuf(st + 1), nxt, pk, alpha, a.c2);
+      if constexpr (!BOUND) T.rescale(alpha);
+    } else {
+      T.template softmax_and_scores<BOUND>(cur, kbuf(st + 1), nxt, pk, alpha, a.c2);
+      if constexpr (!BOUND) T.rescale(alpha);
+      T.pv(vbuf(st), pk);
+      pin_pv<4 * C::DBLK * NQB>();
+    }
+  };
+  typename TT::Scores sn;
+  int st = 0;
+  for (; st + 2 < ns; st += 2) {
+    step(st, sc, sn);
+    step(st + 1, sn, sc);
+  }
+  if (st + 1 < ns) {
+    step(st, sc, sn);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) sc[kb][qb] = sn[kb][qb];
+  }
+  // Last stage (its copy was waited for at the top of the last iteration, or
+  // before the loop when the tile has a single stage).
+  if (LAG && ns > 1) T.pv(vbuf(ns - 2), pk);
+  if (nlast == BK) T.template softmax<BOUND, false>(sc, pk, alpha, BK, a.c2);
+  else T.template softmax<BOUND, true>(sc, pk, alpha, nlast, a.c2);
+  if constexpr (!BOUND) T.rescale(alpha);
+  T.pv(vbuf(ns - 1), pk);
 }
 
 // BOUND selects the softmax path this instantiation runs.  Both are launched
@@ -319,7 +626,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
                                                       const float* __restrict__ k_gmax,
                                                       const float* __restrict__ head_max) {
   using C = Cfg<D, NQB, NW>;
-  __shared__ __attribute__((aligned(16))) u16 smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   int w = blockIdx.x;
@@ -369,9 +676,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     kfac = a.scale * km * kBoundMargin;
   }
 
-  Tile<D, NQB, NW> T;
+  Tile<D, NQB, NW, BOUND> T;
   T.n = lane & 31;
   T.hh = lane >> 5;
+  T.lane = lane;
   const int row0 = wave * 32 * NQB;
   const u16* qh = a.q + b * a.sq[0] + h * a.sq[1];
 #pragma unroll
@@ -382,7 +690,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
 #pragma unroll
     for (int st = 0; st < C::KSTEPS; ++st) {
       bf16x8 z = {};
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 16 * st + 8 * T.hh);
+      bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 16 * st + 8 * T.hh);
+      if constexpr (BOUND) {
+        // bound path: Q * scale * log2(e), rounded to bf16 (nearest even)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          f32x2 f = {(float)x[e] * a.c2, (float)x[e + 1] * a.c2};
+          const bf16x2 b2 = __builtin_convertvector(f, bf16x2);
+          x[e] = b2[0];
+          x[e + 1] = b2[1];
+        }
+      }
       T.qreg[qb][st] = valid ? x : z;
     }
     if constexpr (BOUND) {
@@ -400,7 +718,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
 
   const u16* kh = a.k + b * a.sk[0] + h * a.sk[1];
   const u16* vh = a.v + b * a.sv[0] + h * a.sv[1];
-  run_tile<D, NQB, NW, BOUND>(a, kv_iv, smem, T, kh, vh, e0, e1, tid);
+  // the upper half of the waves runs the lagging order (see run_tile)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  if (wv >= NW / 2) run_tile<D, NQB, NW, BOUND, true>(a, kv_iv, smem, T, kh, vh, e0, e1, wv);
+  else run_tile<D, NQB, NW, BOUND, false>(a, kv_iv, smem, T, kh, vh, e0, e1, wv);
 
   // Epilogue: O = O_acc / l (bf16, nearest even), LSE = m + ln l.
   u16* oh = a.o + b * a.so[0] + h * a.so[1];
@@ -507,6 +828,10 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.head_path_out = head_path_out;
 
   const int grid = blocks->work_order ? blocks->n_work : (int)items;
+  const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
+  if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
+                         : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
+    return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the query tile of this build's kernels");
   if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
     st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true>(a, grid, stream)
                          : launch<64, BOUND_NQB, BOUND_NW, true>(a, grid, stream);

@@ -193,8 +193,9 @@ typedef struct attn_blocks_t {
  *   q_norm, k_gmax, head_max: attn_norms outputs; needed when softmax_mode is
  *       not ATTN_SOFTMAX_ONLINE, ignored (may be NULL) otherwise.
  *   softmax_mode: ATTN_SOFTMAX_*.  The bound shift is
- *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-12);
- *       the factor keeps it above every fp32-computed score.
+ *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-8);
+ *       the factor keeps it above every score the kernel computes (the bound
+ *       path multiplies Q by scale*log2(e) and rounds it to bf16 once).
  *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head.
  * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,
  * bad mode, bad scale), ATTN_E_ALIGN (N % 16, block_q % 16, misaligned pointer
