@@ -13,22 +13,26 @@
 //     is too loose take the running-max path inside the same kernel.
 //
 // gfx950 design (not the TPU kernel's):
-//   * One workgroup per query tile (<= 256 rows), 4 waves x 64 query rows.
-//     A wave holds its Q rows in VGPRs for the whole tile.
+//   * One workgroup per query tile of up to 256 rows of one (batch, head):
+//     8 waves x 32 query rows.  A wave keeps its Q rows in VGPRs for the whole
+//     tile (the bound path keeps Q pre-multiplied by scale*log2(e)).
 //   * S^T = K * Q^T and O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16 (fp32
 //     accumulate).  With that orientation lane (n, h) of a 32x32 accumulator
-//     owns query n and 16 of the 32 keys (or 16 of the 32 output dims), so
-//     the row shift, the row sum and the rescale factor of a query all live
-//     in the lanes that own that query: P feeds the second MFMA straight from
-//     registers, and the bound path needs no cross-lane traffic at all.
-//   * K and V^T stages of 64 keys are staged in LDS, double-buffered, with the
-//     next stage's global loads in flight during the current stage's math.
-//     16-byte chunks are XOR-swizzled so MFMA operand reads are free of bank
-//     conflicts; V is transposed while being written to LDS (keys contiguous
-//     per output dim) so its MFMA operand is one 16-byte LDS read.
-//   * Key tails of 16 tokens use a half-block path chosen per block (the
-//     block's valid count is uniform), never a per-element mask.
-//   * exp is v_exp_f32 on s*scale*log2(e) - m (one FMA + one exp per score).
+//     owns query n, so the row shift, the row sum and the rescale factor of a
+//     query live in the lanes that own it: P feeds the second MFMA straight
+//     from registers and the bound path needs no cross-lane traffic at all.
+//   * Keys stream through LDS in stages of 64 (K and V, [64][D] bf16 each),
+//     four buffers deep with loads issued two stages ahead.  Stages are filled
+//     by LDS-direct buffer loads (global -> LDS, no VGPR round trip); a stage
+//     may gather rows from several intervals, and the last stage of a tile
+//     holds a multiple of 16 keys.  16-byte chunks are XOR-swizzled by row so
+//     both the K reads and the transposing V reads (ds_read_b64_tr_b16) are
+//     free of bank conflicts.
+//   * The upper four waves run half a stage behind the lower four (PV of the
+//     previous stage before QK of this one) so the two halves' MFMA and
+//     exp/VALU phases interleave on each SIMD.
+//   * exp is v_exp_f32 on base-2 scores; the tail stage zeroes the scores of
+//     missing 16-key groups (a per-group select, never a per-element mask).
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
