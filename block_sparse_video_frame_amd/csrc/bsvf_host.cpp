@@ -171,12 +171,16 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
     return fail(ATTN_E_SIZE, "work_order capacity too small");
   }
 
-  // Cost of a tile: rows x attended keys (its share of the useful work).
+  // Cost of a tile: attended keys x max(rows, largest tile / 2).  A tile's
+  // run time follows its key count; a short tile saves time only once it
+  // leaves half of its workgroup's waves idle.
+  int64_t max_rows = 1;
+  for (int32_t t = 0; t < n_qt; ++t) max_rows = std::max<int64_t>(max_rows, q_tiles[2 * t + 1]);
   std::vector<int64_t> cost(n_qt);
   for (int32_t t = 0; t < n_qt; ++t) {
     int64_t keys = 0;
     for (int32_t e = kv_ptr[t]; e < kv_ptr[t + 1]; ++e) keys += kv_iv[2 * e + 1];
-    cost[t] = keys * q_tiles[2 * t + 1];
+    cost[t] = keys * std::max<int64_t>(q_tiles[2 * t + 1], max_rows / 2);
   }
   std::vector<int32_t> order(items);
   std::iota(order.begin(), order.end(), 0);

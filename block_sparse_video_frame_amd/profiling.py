@@ -29,6 +29,8 @@ from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
+    if "fwd_bound_blocks" in kernel:
+        return "attn_fwd[bound]"
     if "fwd_kernel" in kernel:
         return "attn_fwd[bound]" if "true>" in kernel else "attn_fwd[online]"
     if "norms_kernel" in kernel:

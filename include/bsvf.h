@@ -121,8 +121,9 @@ int attn_build_blocks(const attn_pattern_t* p, int32_t block_q,
  * attn_build_schedule — host, integer only, deterministic.
  * Launch order for attn_fwd over batch*heads*n_qt work items (item
  * w = tile + n_qt * (head + heads * batch_index)).  Items are ordered by
- * decreasing cost rows*keys (ties keep the natural order, so tiles sharing
- * their keys stay adjacent), cut into groups of `group` consecutive items, and
+ * decreasing cost keys * max(rows, R/2), R the largest tile's rows (ties keep
+ * the natural order, so tiles sharing their keys stay adjacent), cut into
+ * groups of `group` consecutive items, and
  * group j is placed in the slots of workgroups that the hardware sends to
  * accelerator die j % num_xcd (workgroup i runs on die i % num_xcd).  Unused
  * slots hold -1 (that workgroup exits at once).  The result is a permutation of

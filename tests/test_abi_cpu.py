@@ -115,9 +115,10 @@ def test_schedule_is_a_padded_permutation(name):
         assert (order[order < 0] == -1).all()
         # every die's queue runs longest work first
         cost = {}
+        half = int(blk.q_tiles[:, 1].max()) // 2
         for t in range(blk.n_qt):
             keys = blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum()
-            cost[t] = int(keys) * int(blk.q_tiles[t, 1])
+            cost[t] = int(keys) * max(int(blk.q_tiles[t, 1]), half)
         for x in range(xcd):
             seq = [cost[w % blk.n_qt] for w in order[x::xcd] if w >= 0]
             assert all(a >= b for a, b in zip(seq, seq[1:]))
