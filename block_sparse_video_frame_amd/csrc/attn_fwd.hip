@@ -33,7 +33,6 @@
 //     exp/VALU phases interleave on each SIMD.
 //   * exp is v_exp_f32 on base-2 scores; the tail stage zeroes the scores of
 //     missing 16-key groups (a per-group select, never a per-element mask).
-#include "attn_bound_stage.h"
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
@@ -813,257 +812,6 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   }
 }
 
-// Bound-softmax kernel built from the generated stage blocks
-// (attn_bound_stage.h).  One workgroup = 4 waves x 64 query rows (one wave
-// per SIMD); Q' and the output accumulators stay in AGPRs and every score,
-// probability and operand lives in the VGPRs above the compiler's cap, which
-// the blocks own.  This function keeps the control flow: work item, head
-// path, bound, Q' load, the LDS-direct copies of each stage, barriers, and
-// the epilogue.  Stage s runs one block: the next stage's Q*K^T, this
-// stage's softmax and the P*V products of this and the previous stage (see
-// the generator for the exact schedule).
-template <int D>
-__device__ __forceinline__ void fwd_bound_blocks(const FwdArgs& a, const int32_t* __restrict__ q_tiles,
-                                                 const int32_t* __restrict__ kv_ptr,
-                                                 const int32_t* __restrict__ kv_iv,
-                                                 const int32_t* __restrict__ work_order,
-                                                 const float* __restrict__ k_gmax,
-                                                 const float* __restrict__ head_max) {
-  constexpr int NQB = 2, NW = 4;
-  using C = Cfg<D, NQB, NW>;
-  using BS = BoundStage<D>;
-  // Stage buffers: every LDS byte the CU has (160 KiB) at head_dim 128, so
-  // that copies run two stages ahead of use; more at head_dim 64.
-  constexpr int NBUF = D == 128 ? 5 : 8;
-  constexpr int AHEAD = NBUF - 3;  // stages in flight beyond the three being read
-  __shared__ __attribute__((aligned(16))) u16 smem[NBUF * C::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  int w = blockIdx.x;
-  if (work_order) {
-    if (w >= a.n_work) return;
-    w = work_order[w];
-  }
-  const int total_items = a.n_qt * a.H * a.B;
-  if (w < 0 || w >= total_items) return;
-  const int tile = w % a.n_qt, bh = w / a.n_qt;
-  const int b = bh / a.H, h = bh % a.H;
-  const int qs = q_tiles[2 * tile], nr = q_tiles[2 * tile + 1];
-  if (qs < 0 || nr <= 0 || nr > C::BQ || nr > a.block_q || qs > a.N - nr) return;
-  int e0 = kv_ptr[tile], e1 = kv_ptr[tile + 1];
-  e0 = max(0, min(e0, a.nnz));
-  e1 = max(e0, min(e1, a.nnz));
-
-  bool bound = a.mode == ATTN_SOFTMAX_BOUND_FORCED;
-  if (a.mode == ATTN_SOFTMAX_BOUND) {
-    const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
-    bound = 2.0f * a.scale * mq * mk <= ATTN_ELIGIBLE_NATS;
-  }
-  if (!bound) return;
-  if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = ATTN_PATH_BOUND;
-
-  // Tile-wide max key norm over every attended 16-key granule.
-  float km = 0.0f;
-  {
-    const float* kg = k_gmax + (int64_t)bh * (a.N / 16);
-    for (int e = e0; e < e1; ++e) {
-      const int ks = kv_iv[2 * e], kl = kv_iv[2 * e + 1];
-      if (!interval_ok(ks, kl, a.N)) continue;
-      for (int g = ks / 16 + tid; g < (ks + kl) / 16; g += C::NT) km = fmaxf(km, kg[g]);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) km = fmaxf(km, __shfl_xor(km, m));
-    float* red = reinterpret_cast<float*>(smem);
-    if (lane == 0) red[wave] = km;
-    __syncthreads();
-    km = red[0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) km = fmaxf(km, red[i]);
-    __syncthreads();  // red[] is reused as stage buffer memory below
-  }
-  const float kfac = a.scale * km * kBoundMargin;
-
-  // Q' = Q * scale * log2(e) (bf16, nearest even) into the AGPRs; shift m.
-  const int n = lane & 31, hh = lane >> 5;
-  const int row0 = wave * 32 * NQB;
-  const u16* qh = a.q + b * a.sq[0] + h * a.sq[1];
-  float m2[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int r = row0 + qb * 32 + n;
-    const bool valid = r < nr;
-    const u16* qp = qh + (int64_t)(qs + (valid ? r : 0)) * a.sq[2];
-#pragma unroll
-    for (int st = 0; st < C::KSTEPS; ++st) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 16 * st + 8 * hh);
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        f32x2 f = {(float)x[e] * a.c2, (float)x[e + 1] * a.c2};
-        const bf16x2 b2 = __builtin_convertvector(f, bf16x2);
-        x[e] = b2[0];
-        x[e + 1] = b2[1];
-      }
-      const u32x4 wv = valid ? __builtin_bit_cast(u32x4, x) : u32x4{0u, 0u, 0u, 0u};
-      BS::set_q(qb, st, wv[0], wv[1], wv[2], wv[3]);
-    }
-    const float qn = a.q_norm[(int64_t)bh * a.N + qs + (valid ? r : 0)];
-    m2[qb] = valid ? qn * kfac * kLog2e : 0.0f;
-  }
-  BS::init(-m2[0], -m2[1]);
-
-  // Keys: the tile's intervals cut into 64-key stages, four LDS buffers,
-  // copies issued two stages ahead.
-  const uint32_t ksn = (uint32_t)a.sk[2], vsn = (uint32_t)a.sv[2];
-  const u16* kh = a.k + b * a.sk[0] + h * a.sk[1];
-  const u16* vh = a.v + b * a.sv[0] + h * a.sv[1];
-  const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, 2u * (ksn * (uint32_t)(a.N - 1) + D));
-  const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, 2u * (vsn * (uint32_t)(a.N - 1) + D));
-  int total = 0;
-  for (int e = e0; e < e1; ++e)
-    if (interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) total += kv_iv[2 * e + 1];
-  const bool active = row0 < nr;  // a wave none of whose rows exist only copies
-  if (total > 0) {
-    constexpr int LOADS = 2 * C::LPW;
-    const int ns = (total + BK - 1) / BK, nlast = total - BK * (ns - 1);
-    const LaneOffsets<D> lof = lane_offsets<D>(lane);
-    auto slot = [&](int x) { return (x + NBUF) % NBUF; };
-    auto kbuf = [&](int x) { return smem + slot(x) * C::STAGE; };
-    auto boff = [&](int x) { return (uint32_t)(slot(x) * C::STAGE * 2); };
-    KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
-    kw.seek();
-    DmaLanes<D, NQB, NW> dl;
-    dl.init(ksn, vsn, wave, lane);
-    auto issue = [&](int x) {
-      StageDesc sd;
-      int start;
-      if (kw.next(sd, start)) issue_stage_run<D, NQB, NW>(kbuf(x), kr, vr, dl, ksn, vsn, start, wave);
-      else issue_stage<D, NQB, NW>(kbuf(x), kr, vr, ksn, vsn, sd, wave, lane);
-    };
-    // Copies of stages 0 .. AHEAD-1 first; stage x+AHEAD+1 is issued at the
-    // top of step x, into the buffer that stage x-2 (read last in step x-1)
-    // held.  Copies complete in order, so "stage y landed" is "at most the
-    // copies of later stages still outstanding".
-    const int pre = min(ns, AHEAD + 1);
-    for (int x = 0; x < pre; ++x) issue(x);
-    switch (pre - 1) {  // stage 0 landed
-      case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(wait_vm(LOADS)); break;
-      case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2 * LOADS)); break;
-      case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3 * LOADS)); break;
-      case 4: __builtin_amdgcn_s_waitcnt(wait_vm(4 * LOADS)); break;
-      default: __builtin_amdgcn_s_waitcnt(wait_vm(5 * LOADS)); break;
-    }
-    __syncthreads();
-    if (active) BS::qk0(boff(0) | lof.kl, 0u, 0u, 0u, 0u);
-    for (int s = 0; s < ns; ++s) {
-      // stage s+1 has landed for every wave (copies issued after it may still
-      // be in flight), and every wave is done with the buffer of stage s-2
-      const int later = min(ns - 1, s + AHEAD) - (s + 1);
-      switch (later < 0 ? 0 : later) {
-        case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
-        case 1: __builtin_amdgcn_s_waitcnt(wait_vm(LOADS)); break;
-        case 2: __builtin_amdgcn_s_waitcnt(wait_vm(2 * LOADS)); break;
-        case 3: __builtin_amdgcn_s_waitcnt(wait_vm(3 * LOADS)); break;
-        default: __builtin_amdgcn_s_waitcnt(wait_vm(4 * LOADS)); break;
-      }
-      __syncthreads();
-      if (s + AHEAD + 1 < ns) issue(s + AHEAD + 1);
-      if (!active) continue;
-      const uint32_t kn = boff(s + 1) | lof.kl;
-      const uint32_t vc0 = boff(s) | lof.vl[0], vc1 = boff(s) | lof.vl[1];
-      const uint32_t vp0 = boff(s - 1) | lof.vl[0], vp1 = boff(s - 1) | lof.vl[1];
-      if (s + 1 < ns) {
-        if (s == 0) BS::main_p0_first(kn, vc0, vc1, vp0, vp1);
-        else if (s & 1) BS::main_p1(kn, vc0, vc1, vp0, vp1);
-        else BS::main_p0(kn, vc0, vc1, vp0, vp1);
-      } else if (s == 0) {
-        switch (nlast) {
-          case 16: BS::last_p0_first_n16(kn, vc0, vc1, vp0, vp1); break;
-          case 32: BS::last_p0_first_n32(kn, vc0, vc1, vp0, vp1); break;
-          case 48: BS::last_p0_first_n48(kn, vc0, vc1, vp0, vp1); break;
-          default: BS::last_p0_first_n64(kn, vc0, vc1, vp0, vp1); break;
-        }
-      } else if (s & 1) {
-        switch (nlast) {
-          case 16: BS::last_p1_n16(kn, vc0, vc1, vp0, vp1); break;
-          case 32: BS::last_p1_n32(kn, vc0, vc1, vp0, vp1); break;
-          case 48: BS::last_p1_n48(kn, vc0, vc1, vp0, vp1); break;
-          default: BS::last_p1_n64(kn, vc0, vc1, vp0, vp1); break;
-        }
-      } else {
-        switch (nlast) {
-          case 16: BS::last_p0_n16(kn, vc0, vc1, vp0, vp1); break;
-          case 32: BS::last_p0_n32(kn, vc0, vc1, vp0, vp1); break;
-          case 48: BS::last_p0_n48(kn, vc0, vc1, vp0, vp1); break;
-          default: BS::last_p0_n64(kn, vc0, vc1, vp0, vp1); break;
-        }
-      }
-    }
-  }
-
-  // Epilogue: O = O_acc / l (bf16, nearest even), LSE = m + ln l.
-  float l0, l1;
-  BS::row_sums(l0, l1);
-  const float lpart[NQB] = {l0, l1};
-  u16* oh = a.o + b * a.so[0] + h * a.so[1];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = lpart[qb] + __shfl_xor(lpart[qb], 32);
-    const int r = row0 + qb * 32 + n;
-    const bool valid = r < nr;
-    const float inv = 1.0f / lt;
-    u16* op = oh + (int64_t)(qs + (valid ? r : 0)) * a.so[2];
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) {
-      float acc[16];
-      BS::read_o(qb, db, acc);
-      if (valid) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x2 f0 = {acc[4 * i] * inv, acc[4 * i + 1] * inv};
-          f32x2 f1 = {acc[4 * i + 2] * inv, acc[4 * i + 3] * inv};
-          bf16x2 b0 = __builtin_convertvector(f0, bf16x2), b1 = __builtin_convertvector(f1, bf16x2);
-          u32x2 pk = {__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1)};
-          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * i + 4 * hh) = pk;
-        }
-      }
-    }
-    if (valid && hh == 0) {
-      const int64_t ri = (int64_t)bh * a.N + qs + r;
-      if (a.lse) a.lse[ri] = (m2[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
-      if (a.shift_out) a.shift_out[ri] = m2[qb] * kLn2;
-    }
-  }
-}
-
-// The compiler's VGPR cap must be a literal: one kernel per head size.
-static_assert(BoundStage<128>::kFirstOwnedVgpr == 50, "regenerate: VGPR cap of the head_dim 128 kernel");
-static_assert(BoundStage<64>::kFirstOwnedVgpr == 54, "regenerate: VGPR cap of the head_dim 64 kernel");
-#define BSVF_BOUND_KERNEL(NAME, DIM, CAP)                                                                   \
-  __global__ __launch_bounds__(256) __attribute__((amdgpu_num_vgpr(CAP))) void NAME(                         \
-      FwdArgs a, const int32_t* __restrict__ q_tiles, const int32_t* __restrict__ kv_ptr,                    \
-      const int32_t* __restrict__ kv_iv, const int32_t* __restrict__ work_order,                             \
-      const float* __restrict__ k_gmax, const float* __restrict__ head_max) {                                \
-    fwd_bound_blocks<DIM>(a, q_tiles, kv_ptr, kv_iv, work_order, k_gmax, head_max);                          \
-  }
-BSVF_BOUND_KERNEL(fwd_bound_blocks_d128, 128, 50)
-BSVF_BOUND_KERNEL(fwd_bound_blocks_d64, 64, 54)
-#undef BSVF_BOUND_KERNEL
-
-template <int D>
-int launch_bound_blocks(const FwdArgs& a, int grid, hipStream_t stream) {
-  if constexpr (D == 128)
-    hipLaunchKernelGGL(fwd_bound_blocks_d128, dim3(grid), dim3(256), 0, stream, a,
-                       a.q_tiles, a.kv_ptr, a.kv_iv, a.work_order, a.k_gmax, a.head_max);
-  else
-    hipLaunchKernelGGL(fwd_bound_blocks_d64, dim3(grid), dim3(256), 0, stream, a,
-                       a.q_tiles, a.kv_ptr, a.kv_iv, a.work_order, a.k_gmax, a.head_max);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
-  return ok();
-}
-
 template <int D, int NQB, int NW, bool BOUND>
 int launch(const FwdArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND>), dim3(grid), dim3(64 * NW), 0, stream, a,
@@ -1141,12 +889,13 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.head_path_out = head_path_out;
 
   const int grid = blocks->work_order ? blocks->n_work : (int)items;
-  const int bq_bound = 256, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
+  const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the query tile of this build's kernels");
   if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
-    st = head_dim == 128 ? launch_bound_blocks<128>(a, grid, stream) : launch_bound_blocks<64>(a, grid, stream);
+    st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true>(a, grid, stream)
+                         : launch<64, BOUND_NQB, BOUND_NW, true>(a, grid, stream);
     if (st) return st;
   }
   if (softmax_mode != ATTN_SOFTMAX_BOUND_FORCED) {
