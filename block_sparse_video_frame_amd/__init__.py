@@ -133,7 +133,7 @@ class Blocks:
     def nnz(self) -> int:
         return int(self.kv_iv.shape[0])
 
-    def to_device(self, device, batch: int, heads: int, schedule: bool = True, group: int = 8,
+    def to_device(self, device, batch: int, heads: int, schedule: bool = True, group: int = 0,
                   num_xcd: int = 8) -> "DeviceBlocks":
         import torch
         order = build_schedule(self, batch, heads, group, num_xcd) if schedule else None
@@ -188,7 +188,7 @@ def build_blocks_for(pattern, block_q: int = MAX_BLOCK_Q) -> Blocks:
                         pattern.win_after, tuple(pattern.global_frames), block_q)
 
 
-def build_schedule(blocks: Blocks, batch: int, heads: int, group: int = 8, num_xcd: int = 8) -> np.ndarray:
+def build_schedule(blocks: Blocks, batch: int, heads: int, group: int = 0, num_xcd: int = 8) -> np.ndarray:
     """Launch order of the attention workgroups (``attn_build_schedule``)."""
     L = lib()
     n = ctypes.c_int32(0)

@@ -52,24 +52,32 @@ __global__ __launch_bounds__(kNormThreads) void norms_kernel(NormArgs a) {
 
   float qmax = 0.0f, kmax = 0.0f;
   const int g0 = (blockIdx.x * (kNormThreads / 64) + wave) * kGranulesPerWave;
+  // All of this wave's loads are issued before any arithmetic, so each wave
+  // keeps kGranulesPerWave x 2 x 16 rows in flight.  Granules past the end
+  // re-read the last one (in bounds) and are not stored.
+  u32x4 qv[kGranulesPerWave][IPG], kv[kGranulesPerWave][IPG];
+#pragma unroll
   for (int gi = 0; gi < kGranulesPerWave; ++gi) {
-    const int g = g0 + gi;
-    if (g >= G) break;
-    u32x4 qv[IPG], kv[IPG];
+    const int g = min(g0 + gi, G - 1);
 #pragma unroll
     for (int it = 0; it < IPG; ++it) {
       const int row = g * 16 + it * RPI + rsub;
-      qv[it] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * a.qs_n + 8 * c);
-      kv[it] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * a.ks_n + 8 * c);
+      qv[gi][it] = *reinterpret_cast<const u32x4*>(qh + (int64_t)row * a.qs_n + 8 * c);
+      kv[gi][it] = *reinterpret_cast<const u32x4*>(kh + (int64_t)row * a.ks_n + 8 * c);
     }
+  }
+#pragma unroll
+  for (int gi = 0; gi < kGranulesPerWave; ++gi) {
+    const int g = g0 + gi;
+    if (g >= G) break;
     float kg = 0.0f;
 #pragma unroll
     for (int it = 0; it < IPG; ++it) {
       float sq = 0.0f, sk = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float q0 = bf16lo(qv[it][e]), q1 = bf16hi(qv[it][e]);
-        const float k0 = bf16lo(kv[it][e]), k1 = bf16hi(kv[it][e]);
+        const float q0 = bf16lo(qv[gi][it][e]), q1 = bf16hi(qv[gi][it][e]);
+        const float k0 = bf16lo(kv[gi][it][e]), k1 = bf16hi(kv[gi][it][e]);
         sq = fmaf(q0, q0, sq); sq = fmaf(q1, q1, sq);
         sk = fmaf(k0, k0, sk); sk = fmaf(k1, k1, sk);
       }

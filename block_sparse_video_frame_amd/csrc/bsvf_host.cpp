@@ -157,19 +157,9 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
                         int32_t num_xcd, int32_t* work_order, int32_t* n_work) {
   if (!q_tiles || !kv_ptr || !kv_iv || !n_work) return fail(ATTN_E_INVAL, "NULL argument");
   if (n_qt <= 0 || batch <= 0 || heads <= 0) return fail(ATTN_E_INVAL, "sizes must be positive");
-  if (group < 1 || num_xcd < 1) return fail(ATTN_E_INVAL, "group and num_xcd must be >= 1");
+  if (group < 0 || num_xcd < 1) return fail(ATTN_E_INVAL, "group must be >= 0 and num_xcd >= 1");
   const int64_t items = (int64_t)n_qt * heads * batch;
-  const int64_t per_round = (int64_t)group * num_xcd;
-  const int64_t need = (items + per_round - 1) / per_round * per_round;
-  if (need > 2147483647LL) return fail(ATTN_E_SIZE, "too many work items");
-  if (!work_order) {
-    *n_work = (int32_t)need;
-    return bsvf::ok();
-  }
-  if (*n_work < need) {
-    *n_work = (int32_t)need;
-    return fail(ATTN_E_SIZE, "work_order capacity too small");
-  }
+  if (items > 2147483647LL) return fail(ATTN_E_SIZE, "too many work items");
 
   // Cost of a tile: attended keys x max(rows, largest tile / 2).  A tile's
   // run time follows its key count; a short tile saves time only once it
@@ -182,18 +172,67 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
     for (int32_t e = kv_ptr[t]; e < kv_ptr[t + 1]; ++e) keys += kv_iv[2 * e + 1];
     cost[t] = keys * std::max<int64_t>(q_tiles[2 * t + 1], max_rows / 2);
   }
-  std::vector<int32_t> order(items);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return cost[a % n_qt] > cost[b % n_qt];
-  });
 
-  for (int64_t i = 0; i < need; ++i) work_order[i] = -1;
-  for (int64_t i = 0; i < items; ++i) {
-    const int64_t j = i / group, r = i % group;
-    const int64_t xcd = j % num_xcd, slot = (j / num_xcd) * group + r;
-    work_order[slot * num_xcd + xcd] = order[i];
+  // One queue of items per die; workgroup slot*num_xcd + x takes item
+  // queue[x][slot].
+  std::vector<std::vector<int32_t>> queue(num_xcd);
+  if (group > 0) {
+    // Items by decreasing cost (stable), dealt to the dies in groups of `group`.
+    std::vector<int32_t> order(items);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return cost[a % n_qt] > cost[b % n_qt];
+    });
+    for (int64_t i = 0; i < items; ++i) queue[(i / group) % num_xcd].push_back(order[i]);
+  } else {
+    // Tiles of one (batch, head) with the same key intervals (the tiles of one
+    // query frame) read the same K and V: keep each such set together on one
+    // die, so its tiles stream those keys through that die's L2 at the same
+    // time.  Sets go, heaviest first, to the die with the least work so far.
+    struct Set { int64_t cost; int32_t first; std::vector<int32_t> items; };
+    std::vector<Set> sets;
+    for (int64_t bh = 0; bh < (int64_t)batch * heads; ++bh) {
+      int32_t t = 0;
+      while (t < n_qt) {
+        Set st{0, (int32_t)(bh * n_qt + t), {}};
+        int32_t u = t;
+        for (; u < n_qt; ++u) {
+          const int32_t n0 = kv_ptr[t + 1] - kv_ptr[t], n1 = kv_ptr[u + 1] - kv_ptr[u];
+          if (n0 != n1 || !std::equal(kv_iv + 2 * kv_ptr[t], kv_iv + 2 * kv_ptr[t + 1], kv_iv + 2 * kv_ptr[u]))
+            break;
+          st.items.push_back((int32_t)(bh * n_qt + u));
+          st.cost += cost[u];
+        }
+        sets.push_back(std::move(st));
+        t = u;
+      }
+    }
+    std::stable_sort(sets.begin(), sets.end(), [](const Set& a, const Set& b) { return a.cost > b.cost; });
+    std::vector<int64_t> load(num_xcd, 0);
+    for (const Set& st : sets) {
+      int x = 0;
+      for (int j = 1; j < num_xcd; ++j)
+        if (load[j] < load[x]) x = j;
+      load[x] += st.cost;
+      queue[x].insert(queue[x].end(), st.items.begin(), st.items.end());
+    }
   }
+  size_t depth = 0;
+  for (const auto& q : queue) depth = std::max(depth, q.size());
+  if (group > 0) depth = (size_t)((depth + group - 1) / group * group);
+  const int64_t need = (int64_t)depth * num_xcd;
+  if (need > 2147483647LL) return fail(ATTN_E_SIZE, "too many work items");
+  if (!work_order) {
+    *n_work = (int32_t)need;
+    return bsvf::ok();
+  }
+  if (*n_work < need) {
+    *n_work = (int32_t)need;
+    return fail(ATTN_E_SIZE, "work_order capacity too small");
+  }
+  for (int64_t i = 0; i < need; ++i) work_order[i] = -1;
+  for (int x = 0; x < num_xcd; ++x)
+    for (size_t slot = 0; slot < queue[x].size(); ++slot) work_order[slot * num_xcd + x] = queue[x][slot];
   *n_work = (int32_t)need;
   return bsvf::ok();
 }

@@ -120,18 +120,23 @@ int attn_build_blocks(const attn_pattern_t* p, int32_t block_q,
 /*
  * attn_build_schedule — host, integer only, deterministic.
  * Launch order for attn_fwd over batch*heads*n_qt work items (item
- * w = tile + n_qt * (head + heads * batch_index)).  Items are ordered by
- * decreasing cost keys * max(rows, R/2), R the largest tile's rows (ties keep
- * the natural order, so tiles sharing their keys stay adjacent), cut into
- * groups of `group` consecutive items, and
- * group j is placed in the slots of workgroups that the hardware sends to
- * accelerator die j % num_xcd (workgroup i runs on die i % num_xcd).  Unused
- * slots hold -1 (that workgroup exits at once).  The result is a permutation of
+ * w = tile + n_qt * (head + heads * batch_index)).  A tile's cost is
+ * keys * max(rows, R/2), R the largest tile's rows.  Workgroup i runs on
+ * accelerator die i % num_xcd and takes the next item of that die's queue:
+ *   group > 0: items by decreasing cost (ties keep the natural order), cut
+ *     into groups of `group` consecutive items, group j appended to die
+ *     j % num_xcd;
+ *   group == 0: the tiles of one (batch, head) that share their key
+ *     intervals (one query frame's tiles) form a set that stays together on
+ *     one die, so they stream the same K and V through that die's L2; sets,
+ *     heaviest first, go to the die with the least cost so far.
+ * Queues are padded with -1 to a common depth (a multiple of `group` when
+ * group > 0); such a workgroup exits at once.  The result is a permutation of
  * all items plus padding; it changes only the execution order, never results.
  * Inputs are the host block list from attn_build_blocks.  Two-call protocol:
  * with work_order NULL only *n_work is written; otherwise *n_work is the
  * capacity (ATTN_E_SIZE if short, needed count written back).
- * Errors: ATTN_E_INVAL (NULL arrays, non-positive sizes, group < 1,
+ * Errors: ATTN_E_INVAL (NULL arrays, non-positive sizes, group < 0,
  * num_xcd < 1), ATTN_E_SIZE.
  */
 int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr,

@@ -127,10 +127,53 @@ def test_schedule_is_a_padded_permutation(name):
     assert (o1 == o2).all()
 
 
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_frame_set_schedule(name):
+    """group 0: a permutation; each set of tiles with equal key intervals of one
+    head sits contiguously on a single die; die loads balanced within one set."""
+    wl = WORKLOADS[name]
+    blk = bs.build_blocks_for(wl.pattern, 256)
+    items = blk.n_qt * wl.heads * wl.batch
+    xcd = 8
+    order = bs.build_schedule(blk, wl.batch, wl.heads, 0, xcd)
+    assert len(order) % xcd == 0
+    real = order[order >= 0]
+    assert sorted(real.tolist()) == list(range(items))
+    half = int(blk.q_tiles[:, 1].max()) // 2
+    key = {}
+    cost = {}
+    for t in range(blk.n_qt):
+        ivs = tuple(map(tuple, blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1]].tolist()))
+        key[t] = ivs
+        cost[t] = int(blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum()) * max(int(blk.q_tiles[t, 1]), half)
+    loads, biggest = [], 0
+    seen = set()
+    for x in range(xcd):
+        q = [w for w in order[x::xcd] if w >= 0]
+        assert all(w == -1 for w in order[x::xcd][len(q):])       # padding only at the end
+        loads.append(sum(cost[w % blk.n_qt] for w in q))
+        runs = []
+        for w in q:
+            s = (w // blk.n_qt, key[w % blk.n_qt])
+            if not runs or runs[-1] != s:
+                runs.append(s)
+        assert len(runs) == len(set(runs))                        # each set contiguous
+        assert not (set(runs) & seen)                             # and on one die only
+        seen |= set(runs)
+    sets = {}
+    for w in range(items):
+        s = (w // blk.n_qt, key[w % blk.n_qt])
+        sets[s] = sets.get(s, 0) + cost[w % blk.n_qt]
+    biggest = max(sets.values())
+    assert max(loads) - min(loads) <= biggest
+
+
 def test_schedule_errors():
     blk = bs.build_blocks(3, 32, 1, 1, (), 32)
     with pytest.raises(bs.AttnError):
-        bs.build_schedule(blk, 1, 1, 0, 8)
+        bs.build_schedule(blk, 1, 1, -1, 8)
+    with pytest.raises(bs.AttnError):
+        bs.build_schedule(blk, 1, 1, 4, 0)
     with pytest.raises(bs.AttnError):
         bs.build_schedule(blk, 0, 1, 4, 8)
 
