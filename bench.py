@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with fallback, 2 forced bound")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", default="aligned16", choices=["aligned16", "granular128"],
+                    help="block layout: frame-aligned 16-token blocks (the method), or fixed 128-token "
+                         "blocks that ignore frame edges with a per-element frame mask (ablation)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for the byte counters)")
     args = ap.parse_args()
@@ -125,7 +128,7 @@ def main():
     B, H, N, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] workload {wl.name}: B{B} H{H} N{N} D{D} mode {args.mode}", file=sys.stderr, flush=True)
+    print(f"[bench] workload {wl.name}: B{B} H{H} N{N} D{D} mode {args.mode} layout {args.layout}", file=sys.stderr, flush=True)
     qb, kb, vb = make_qkv(wl)
 
     def up(bits):
@@ -133,7 +136,10 @@ def main():
 
     q, k, v = up(qb), up(kb), up(vb)
     t0 = time.perf_counter()
-    blocks = bs.build_blocks_for(wl.pattern, bs.MAX_BLOCK_Q)
+    if args.layout == "aligned16":
+        blocks = bs.build_blocks_for(wl.pattern, bs.MAX_BLOCK_Q)
+    else:
+        blocks = bs.build_blocks_granular(wl.pattern, 128, bs.MAX_BLOCK_Q)
     setup_ms = (time.perf_counter() - t0) * 1e3
     dblk = blocks.to_device(dev, B, H)
     useful_flop = 4.0 * D * blocks.useful_pairs * B * H
@@ -192,7 +198,7 @@ def main():
     value = useful_flop / (ms_step * 1e-3) / 1e12
     fwd_tflops = useful_flop / (fwd_ms * 1e-3) / 1e12
     norms_bytes = 2 * B * H * N * D * 2 + 4 * B * H * (N + N // 16 + 2)
-    traffic = load_traffic(wl.name, args.mode)
+    traffic = load_traffic(wl.name, args.mode) if args.layout == "aligned16" else None
     res = {
         "metric": "useful TFLOP/s (unmasked blocks) block-sparse attn fwd; % bf16 MFMA peak",
         "value": round(value, 2),
@@ -209,7 +215,7 @@ def main():
         "config": {"workload": f"{wl.name} chunk: B{B} H{H} D{D}, {wl.pattern.num_frames} frames x "
                                f"{wl.pattern.tokens_per_frame} tokens (N {N}), window -{wl.pattern.win_before}/"
                                f"+{wl.pattern.win_after}, global {list(wl.pattern.global_frames)}",
-                   "softmax_mode": args.mode, "block_q": bs.MAX_BLOCK_Q,
+                   "softmax_mode": args.mode, "block_q": bs.MAX_BLOCK_Q, "layout": args.layout,
                    "useful_flop": useful_flop, "useful_pairs_per_head": blocks.useful_pairs},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attn_fwd_ms": round(fwd_ms, 4),

@@ -15,6 +15,7 @@ block_sparse_video_frame_amd.build``); without it every call raises.
 from __future__ import annotations
 
 import ctypes
+from typing import Optional
 import math
 import os
 from dataclasses import dataclass
@@ -24,7 +25,7 @@ import numpy as np
 __all__ = [
     "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "PATH_ONLINE", "PATH_BOUND",
     "MAX_BLOCK_Q", "ELIGIBLE_NATS", "AttnError", "lib", "library_path", "abi_version",
-    "Blocks", "DeviceBlocks", "build_blocks", "build_schedule", "norms", "attention",
+    "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "attention",
 ]
 
 SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED = 0, 1, 2
@@ -85,12 +86,20 @@ def lib():
     L.attn_build_blocks.restype = ctypes.c_int
     L.attn_build_blocks.argtypes = [ctypes.POINTER(_Pattern), ctypes.c_int32, _I32P, _I32P, _I32P,
                                     _I64P, _I32P, _I32P]
+    L.attn_build_blocks_granular.restype = ctypes.c_int
+    L.attn_build_blocks_granular.argtypes = [ctypes.POINTER(_Pattern), ctypes.c_int32, ctypes.c_int32, _I32P,
+                                             _I32P, _I32P, _I32P, _I64P, _I32P, _I32P]
     L.attn_build_schedule.restype = ctypes.c_int
     L.attn_build_schedule.argtypes = [_I32P, _I32P, _I32P, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P]
     L.attn_norms.restype = ctypes.c_int
     L.attn_norms.argtypes = [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                              _I64P, _I64P, _VP, _VP, _VP, _VP]
+    L.attn_fwd_masked.restype = ctypes.c_int
+    L.attn_fwd_masked.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.c_float,
+                                  ctypes.POINTER(_Blocks), _VP, ctypes.POINTER(_Pattern), _VP, _VP, _VP,
+                                  ctypes.c_int32, _VP, _VP]
     L.attn_fwd.restype = ctypes.c_int
     L.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.c_float,
@@ -124,6 +133,8 @@ class Blocks:
     useful_pairs: int     # unmasked (query, key) pairs of one head
     block_q: int
     seq_len: int
+    kv_flag: Optional[np.ndarray] = None  # [nnz] int32, frame-unaware layout only
+    pattern: object = None                # the pattern of a frame-unaware layout
 
     @property
     def n_qt(self) -> int:
@@ -142,7 +153,8 @@ class Blocks:
             return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
         return DeviceBlocks(self, up(self.q_tiles), up(self.kv_ptr), up(self.kv_iv),
-                            up(order) if order is not None else None, batch, heads)
+                            up(order) if order is not None else None, batch, heads,
+                            up(self.kv_flag) if self.kv_flag is not None else None)
 
 
 @dataclass
@@ -154,6 +166,7 @@ class DeviceBlocks:
     work_order: object
     batch: int
     heads: int
+    kv_flag: object = None
 
     def c_struct(self) -> _Blocks:
         return _Blocks(self.q_tiles.data_ptr(), self.kv_ptr.data_ptr(), self.kv_iv.data_ptr(),
@@ -180,6 +193,29 @@ def build_blocks(num_frames: int, tokens_per_frame: int, win_before: int, win_af
     _check(L.attn_build_blocks(ctypes.byref(p), block_q, _i32(qt), _i32(kp), _i32(kv),
                                ctypes.byref(useful), ctypes.byref(n_qt), ctypes.byref(nnz)))
     return Blocks(qt, kp, kv, int(useful.value), block_q, num_frames * tokens_per_frame)
+
+
+def build_blocks_granular(pattern, granule: int = 128, block_q: int = MAX_BLOCK_Q) -> Blocks:
+    """Block list of the frame-unaware layout (``attn_build_blocks_granular``):
+    fixed tiles and key blocks that ignore frame edges, with ``kv_flag`` marking
+    the partly masked runs."""
+    L = lib()
+    g = np.ascontiguousarray(np.asarray(tuple(pattern.global_frames), dtype=np.int32).reshape(-1))
+    p = _Pattern(pattern.num_frames, pattern.tokens_per_frame, pattern.win_before, pattern.win_after,
+                 len(g), _i32(g) if len(g) else None)
+    n_qt = ctypes.c_int32(0)
+    nnz = ctypes.c_int32(0)
+    useful = ctypes.c_int64(0)
+    _check(L.attn_build_blocks_granular(ctypes.byref(p), granule, block_q, None, None, None, None,
+                                        ctypes.byref(useful), ctypes.byref(n_qt), ctypes.byref(nnz)))
+    qt = np.zeros((n_qt.value, 2), np.int32)
+    kp = np.zeros(n_qt.value + 1, np.int32)
+    kv = np.zeros((nnz.value, 2), np.int32)
+    fl = np.zeros(nnz.value, np.int32)
+    _check(L.attn_build_blocks_granular(ctypes.byref(p), granule, block_q, _i32(qt), _i32(kp), _i32(kv), _i32(fl),
+                                        ctypes.byref(useful), ctypes.byref(n_qt), ctypes.byref(nnz)))
+    return Blocks(qt, kp, kv, int(useful.value), block_q, pattern.num_frames * pattern.tokens_per_frame,
+                  kv_flag=fl, pattern=pattern)
 
 
 def build_blocks_for(pattern, block_q: int = MAX_BLOCK_Q) -> Blocks:
@@ -239,7 +275,8 @@ norms = _norms
 
 def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: int = SOFTMAX_BOUND,
               norms=None, out=None, lse=None, shift_out=None, head_path=None):
-    """Block-sparse attention forward (``attn_fwd``); returns ``(out, lse)``.
+    """Block-sparse attention forward (``attn_fwd``; ``attn_fwd_masked`` for
+    blocks of :func:`build_blocks_granular`); returns ``(out, lse)``.
 
     ``norms``: the ``(q_norm, k_gmax, head_max)`` triple from :func:`norms`
     (computed here when the mode needs it and none is given).
@@ -259,8 +296,19 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
     st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
     cb = blocks.c_struct()
     qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
-    _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          shift_out.data_ptr() if shift_out is not None else None,
-                          B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb), qn, kg, hm, mode,
-                          head_path.data_ptr() if head_path is not None else None, _stream(q)))
+    so = shift_out.data_ptr() if shift_out is not None else None
+    hp = head_path.data_ptr() if head_path is not None else None
+    if blocks.kv_flag is None:
+        _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), so,
+                              B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb), qn, kg, hm, mode,
+                              hp, _stream(q)))
+    else:
+        pat = blocks.host.pattern
+        g = np.ascontiguousarray(np.asarray(tuple(pat.global_frames), dtype=np.int32).reshape(-1))
+        p = _Pattern(pat.num_frames, pat.tokens_per_frame, pat.win_before, pat.win_after, len(g),
+                     _i32(g) if len(g) else None)
+        _check(lib().attn_fwd_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     so, B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb),
+                                     blocks.kv_flag.data_ptr(), ctypes.byref(p), qn, kg, hm, mode, hp,
+                                     _stream(q)))
     return out, lse

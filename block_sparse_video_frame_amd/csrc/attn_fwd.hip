@@ -81,6 +81,11 @@ struct FwdArgs {
   const float* head_max;
   int32_t mode;
   int32_t* head_path_out;
+  // frame mask of the frame-unaware layout (kernels built with MASK only)
+  const int32_t* kv_flag;   // per interval: 1 = some (row, key) pair masked
+  int32_t frame_T;          // tokens per frame
+  int32_t win_lo, win_hi;   // key frame - query frame allowed in [win_lo, win_hi]
+  uint32_t gbits[2];        // global key frames, bit f of the 64-bit word
 };
 
 
@@ -301,6 +306,7 @@ struct Tile {
   float m2[NQB];    // row shift in log2 units (bound: fixed; online: running max)
   float lsum[NQB];  // this lane half's share of the row sum
   int n, hh, lane;
+  int fq[NQB];  // frame of this lane's query row (frame-unaware layout only)
   LaneOffsets<D> lof;
   static constexpr uint32_t RS = 2 * D;
 
@@ -354,11 +360,14 @@ struct Tile {
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m2[qb], mx * c2);
-        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - mnew);
+        // a row none of whose keys so far is attended (frame-unaware layout)
+        // keeps m = -inf; shift by 0 then, so that nothing becomes NaN
+        const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - msafe);
         m2[qb] = mnew;
         lsum[qb] *= alpha[qb];
       }
-      const float nm = -m2[qb];
+      const float nm = m2[qb] == -INFINITY ? 0.0f : -m2[qb];
       float p[2][16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -415,11 +424,14 @@ struct Tile {
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][qb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m2[qb], mx * c2);
-        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - mnew);
+        // a row none of whose keys so far is attended (frame-unaware layout)
+        // keeps m = -inf; shift by 0 then, so that nothing becomes NaN
+        const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+        alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - msafe);
         m2[qb] = mnew;
         lsum[qb] *= alpha[qb];
       }
-      nm[qb] = -m2[qb];
+      nm[qb] = m2[qb] == -INFINITY ? 0.0f : -m2[qb];
     }
     // MFMA i accumulates block kbn(i) of the next stage: the first half of the
     // chunks fills block 1 while block 0 of `cur` is being consumed, the second
@@ -482,6 +494,34 @@ struct Tile {
         for (int kst = 0; kst < 2; ++kst) {
           u32x4 w = {pw[qb][kb][4 * kst], pw[qb][kb][4 * kst + 1], pw[qb][kb][4 * kst + 2], pw[qb][kb][4 * kst + 3]};
           pk[qb][kb][kst] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+  }
+
+  // Frame mask of one stage of the frame-unaware layout: keys k0 .. k0+63 (a
+  // contiguous run; at most one frame edge in it as tokens_per_frame >= 64).
+  // Scores of keys this lane's row may not attend, and of positions at or
+  // past `nvalid`, become -inf.  Key position p = 32kb + 8i + 4hh + j holds
+  // register 4i + j of block kb.
+  __device__ __forceinline__ void apply_mask(Scores& s, const FwdArgs& a, int k0, int nvalid) const {
+    const int T = a.frame_T;
+    const int f0 = k0 / T;
+    const int edge = (f0 + 1) * T - k0;  // first position in frame f0 + 1
+    const uint64_t gb = (uint64_t)a.gbits[0] | ((uint64_t)a.gbits[1] << 32);
+    const bool g0 = f0 < 64 && ((gb >> f0) & 1), g1 = f0 + 1 < 64 && ((gb >> (f0 + 1)) & 1);
+    const int thr = edge - 4 * hh, lim = nvalid - 4 * hh;
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const int d = f0 - fq[qb];
+      const bool ok0 = (d >= a.win_lo && d <= a.win_hi) || g0;
+      const bool ok1 = (d + 1 >= a.win_lo && d + 1 <= a.win_hi) || g1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int pb = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const bool keep = (pb >= thr ? ok1 : ok0) && pb < lim;
+          s[kb][qb][r] = keep ? s[kb][qb][r] : -INFINITY;
         }
     }
   }
@@ -576,6 +616,26 @@ struct KeyWalker {
   }
 };
 
+// The start key and mask flag of the stages in the order they are consumed
+// (the frame-unaware layout, whose stages each lie inside one interval).
+struct StageCursor {
+  const int32_t* __restrict__ kv_iv;
+  const int32_t* __restrict__ kv_flag;
+  int e, e1, N, cs, cl, off;
+  bool flag;
+
+  __device__ __forceinline__ void seek() {
+    while (e < e1 && !interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], N)) ++e;
+    if (e < e1) { cs = kv_iv[2 * e]; cl = kv_iv[2 * e + 1]; off = 0; flag = kv_flag[e] != 0; }
+  }
+  __device__ __forceinline__ void next(int& k0, bool& masked) {
+    k0 = cs + off;
+    masked = flag;
+    off += BK;
+    if (off >= cl) { ++e; seek(); }
+  }
+};
+
 // Software-pipelined walk over the tile's stages with kBuffers LDS buffers
 // (stage x lives in buffer x mod kBuffers).  Per iteration s, after one
 // barrier, stage s+kPrefetch starts streaming in, and each wave runs F(s) --
@@ -585,7 +645,7 @@ struct KeyWalker {
 // lagging half does P(s-1) then F(s).  One wave's vector work then overlaps
 // the other's matrix work instead of both contending for the same unit.
 // Every stage but the tile's last is full.
-template <int D, int NQB, int NW, bool BOUND, bool LAG>
+template <int D, int NQB, int NW, bool BOUND, bool LAG, bool MASK>
 __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
                                          Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh,
                                          int e0, int e1, int wave, bool active) {
@@ -607,6 +667,17 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
   const lds_char* sm = lds_bytes(smem);
   KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
   kw.seek();
+  StageCursor cur_stage{kv_iv, a.kv_flag, e0, e1, a.N, 0, 0, 0, false};
+  if constexpr (MASK) cur_stage.seek();
+  // frame mask of stage x (consumed in order), before its softmax
+  auto mask_stage = [&](typename Tile<D, NQB, NW, BOUND>::Scores& sc_x, int x) {
+    if constexpr (MASK) {
+      int k0;
+      bool masked;
+      cur_stage.next(k0, masked);
+      if (masked) T.apply_mask(sc_x, a, k0, x == ns - 1 ? nlast : BK);
+    }
+  };
   DmaLanes<D, NQB, NW> dl;
   dl.init(ksn, vsn, wave, T.lane);
   auto issue = [&](int x) {
@@ -634,6 +705,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
     __syncthreads();
     if (st + kPrefetch < ns) issue(st + kPrefetch);
     if (!active) return;
+    mask_stage(cur, st);
     if constexpr (LAG) {
       if (st > 0) {
         T.pv(sm, boff(st - 1), pk);
@@ -664,6 +736,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
   // Last stage (its copy was waited for at the top of the last iteration, or
   // before the loop when the tile has a single stage).
   if (!active) return;
+  mask_stage(sc, ns - 1);
   if (LAG && ns > 1) T.pv(sm, boff(ns - 2), pk);
   if (nlast == BK) T.template softmax<BOUND, false>(sc, pk, alpha, BK, a.c2);
   else T.template softmax<BOUND, true>(sc, pk, alpha, nlast, a.c2);
@@ -675,7 +748,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
 // over the same work; a workgroup whose head takes the other path exits at
 // once, so each head is computed by exactly one of them and each path gets a
 // register allocation of its own.
-template <int D, int NQB, int NW, bool BOUND>
+template <int D, int NQB, int NW, bool BOUND, bool MASK>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* __restrict__ q_tiles,
                                                       const int32_t* __restrict__ kv_ptr,
                                                       const int32_t* __restrict__ kv_iv,
@@ -781,8 +854,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   // A wave none of whose rows exist (the short last tile of a frame) keeps
   // its share of the loads and barriers but skips the math.
   const bool active = wv * 32 * NQB < nr;
-  if (wv >= NW / 2) run_tile<D, NQB, NW, BOUND, true>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
-  else run_tile<D, NQB, NW, BOUND, false>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+  if constexpr (MASK) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) T.fq[qb] = (qs + min(row0 + qb * 32 + T.n, nr - 1)) / a.frame_T;
+  }
+  if (wv >= NW / 2) run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+  else run_tile<D, NQB, NW, BOUND, false, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
 
   // Epilogue: O = O_acc / l (bf16, nearest even), LSE = m + ln l.
   u16* oh = a.o + b * a.so[0] + h * a.so[1];
@@ -812,9 +889,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   }
 }
 
-template <int D, int NQB, int NW, bool BOUND>
+template <int D, int NQB, int NW, bool BOUND, bool MASK>
 int launch(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND>), dim3(grid), dim3(64 * NW), 0, stream, a,
+  hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a,
                      a.q_tiles, a.kv_ptr, a.kv_iv, a.work_order, a.k_gmax, a.head_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
@@ -826,12 +903,12 @@ int launch(const FwdArgs& a, int grid, hipStream_t stream) {
 
 using namespace bsvf;
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
-                        int32_t head_dim, const int64_t* strides, float scale,
-                        const attn_blocks_t* blocks, const float* q_norm, const float* k_gmax,
-                        const float* head_max, int32_t softmax_mode, int32_t* head_path_out,
-                        hipStream_t stream) {
+static int fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, float* shift_out,
+                     int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim, const int64_t* strides,
+                     float scale, const attn_blocks_t* blocks, const int32_t* kv_flag,
+                     const attn_pattern_t* pattern, const float* q_norm, const float* k_gmax,
+                     const float* head_max, int32_t softmax_mode, int32_t* head_path_out, hipStream_t stream) {
+  const bool masked = pattern != nullptr;
   if (batch <= 0 || heads <= 0 || seq_len <= 0) return fail(ATTN_E_INVAL, "sizes must be positive");
   if (head_dim != 64 && head_dim != 128) return fail(ATTN_E_UNSUPPORTED, "head_dim must be 64 or 128");
   if (seq_len % 16) return fail(ATTN_E_ALIGN, "seq_len must be a multiple of 16");
@@ -852,6 +929,22 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (blocks->work_order && blocks->n_work <= 0) return fail(ATTN_E_INVAL, "n_work must be positive");
   if (softmax_mode != ATTN_SOFTMAX_ONLINE && (!q_norm || !k_gmax || !head_max))
     return fail(ATTN_E_UNSUPPORTED, "bound softmax needs q_norm, k_gmax and head_max");
+  uint64_t gbits = 0;
+  if (masked) {
+    if (!kv_flag) return fail(ATTN_E_INVAL, "kv_flag is NULL");
+    if (pattern->tokens_per_frame < 64) return fail(ATTN_E_UNSUPPORTED, "the frame mask needs tokens_per_frame >= 64");
+    if ((int64_t)pattern->num_frames * pattern->tokens_per_frame != seq_len)
+      return fail(ATTN_E_PATTERN, "num_frames * tokens_per_frame must equal seq_len");
+    if (pattern->win_before < 0 || pattern->win_after < 0) return fail(ATTN_E_PATTERN, "windows must be >= 0");
+    if (pattern->num_global < 0 || (pattern->num_global > 0 && !pattern->global_frames))
+      return fail(ATTN_E_INVAL, "bad global frame list");
+    for (int32_t i = 0; i < pattern->num_global; ++i) {
+      const int32_t g = pattern->global_frames[i];
+      if (g < 0 || g >= pattern->num_frames) return fail(ATTN_E_PATTERN, "global frame out of range");
+      if (g >= 64) return fail(ATTN_E_UNSUPPORTED, "global frames must be below 64");
+      gbits |= (uint64_t)1 << g;
+    }
+  }
   const int64_t items = (int64_t)blocks->n_qt * heads * batch;
   if (items > 2147483647LL) return fail(ATTN_E_SIZE, "too many work items");
   if ((int64_t)batch * heads * seq_len > 2147483647LL) return fail(ATTN_E_SIZE, "B*H*N exceeds INT32_MAX");
@@ -887,6 +980,12 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   a.head_max = head_max;
   a.mode = softmax_mode;
   a.head_path_out = head_path_out;
+  a.kv_flag = kv_flag;
+  a.frame_T = masked ? pattern->tokens_per_frame : 0;
+  a.win_lo = masked ? -pattern->win_before : 0;
+  a.win_hi = masked ? pattern->win_after : 0;
+  a.gbits[0] = (uint32_t)gbits;
+  a.gbits[1] = (uint32_t)(gbits >> 32);
 
   const int grid = blocks->work_order ? blocks->n_work : (int)items;
   const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
@@ -894,14 +993,44 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the query tile of this build's kernels");
   if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
-    st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true>(a, grid, stream)
-                         : launch<64, BOUND_NQB, BOUND_NW, true>(a, grid, stream);
+    if (masked)
+      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
+                           : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream);
+    else
+      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, false>(a, grid, stream)
+                           : launch<64, BOUND_NQB, BOUND_NW, true, false>(a, grid, stream);
     if (st) return st;
   }
   if (softmax_mode != ATTN_SOFTMAX_BOUND_FORCED) {
-    st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false>(a, grid, stream)
-                         : launch<64, ONLINE_NQB, ONLINE_NW, false>(a, grid, stream);
+    if (masked)
+      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, stream)
+                           : launch<64, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, stream);
+    else
+      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, stream)
+                           : launch<64, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, stream);
     if (st) return st;
   }
   return ok();
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+                        int32_t head_dim, const int64_t* strides, float scale,
+                        const attn_blocks_t* blocks, const float* q_norm, const float* k_gmax,
+                        const float* head_max, int32_t softmax_mode, int32_t* head_path_out,
+                        hipStream_t stream) {
+  return fwd_entry(q, k, v, o, lse, shift_out, batch, heads, seq_len, head_dim, strides, scale, blocks,
+                   nullptr, nullptr, q_norm, k_gmax, head_max, softmax_mode, head_path_out, stream);
+}
+
+extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                               float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+                               int32_t head_dim, const int64_t* strides, float scale,
+                               const attn_blocks_t* blocks, const int32_t* kv_flag,
+                               const attn_pattern_t* pattern, const float* q_norm,
+                               const float* k_gmax, const float* head_max, int32_t softmax_mode,
+                               int32_t* head_path_out, hipStream_t stream) {
+  if (!pattern) return fail(ATTN_E_INVAL, "pattern is NULL");
+  return fwd_entry(q, k, v, o, lse, shift_out, batch, heads, seq_len, head_dim, strides, scale, blocks,
+                   kv_flag, pattern, q_norm, k_gmax, head_max, softmax_mode, head_path_out, stream);
 }

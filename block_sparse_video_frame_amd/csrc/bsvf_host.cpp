@@ -152,6 +152,92 @@ int attn_build_blocks(const attn_pattern_t* p, int32_t block_q, int32_t* q_tiles
   return bsvf::ok();
 }
 
+int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t block_q,
+                               int32_t* q_tiles, int32_t* kv_ptr, int32_t* kv_iv, int32_t* kv_flag,
+                               int64_t* useful_pairs, int32_t* n_qt, int32_t* nnz) {
+  if (!p || !n_qt || !nnz) return fail(ATTN_E_INVAL, "pattern, n_qt and nnz must not be NULL");
+  const int64_t F = p->num_frames, T = p->tokens_per_frame;
+  if (F < 1) return fail(ATTN_E_PATTERN, "num_frames must be >= 1");
+  if (T <= 0 || T % 16) return fail(ATTN_E_ALIGN, "tokens_per_frame must be a positive multiple of 16");
+  if (granule <= 0 || granule % 64) return fail(ATTN_E_ALIGN, "granule must be a positive multiple of 64");
+  if (block_q <= 0 || block_q % 16) return fail(ATTN_E_ALIGN, "block_q must be a positive multiple of 16");
+  if (p->win_before < 0 || p->win_after < 0) return fail(ATTN_E_PATTERN, "windows must be >= 0");
+  if (p->num_global < 0) return fail(ATTN_E_PATTERN, "num_global must be >= 0");
+  if (p->num_global > 0 && !p->global_frames) return fail(ATTN_E_INVAL, "global_frames is NULL");
+  if (F * T > 2147483647LL) return fail(ATTN_E_SIZE, "num_frames * tokens_per_frame exceeds INT32_MAX");
+  std::vector<char> is_global(F, 0);
+  for (int32_t i = 0; i < p->num_global; ++i) {
+    const int32_t g = p->global_frames[i];
+    if (g < 0 || g >= F) return fail(ATTN_E_PATTERN, "global frame out of range");
+    is_global[g] = 1;
+  }
+  auto attends = [&](int64_t f, int64_t g) {
+    return (g - f >= -(int64_t)p->win_before && g - f <= (int64_t)p->win_after) || is_global[g];
+  };
+  const int64_t N = F * T;
+  // Blocks of one tile: 0 none, 1 every (row, key) pair attended, 2 some.
+  auto block_kind = [&](int64_t qs, int64_t qe, int64_t ks, int64_t ke) {
+    bool any = false, all = true;
+    for (int64_t f = qs / T; f <= (qe - 1) / T; ++f)
+      for (int64_t g = ks / T; g <= (ke - 1) / T; ++g) {
+        const bool a = attends(f, g);
+        any |= a;
+        all &= a;
+      }
+    return any ? (all ? 1 : 2) : 0;
+  };
+  int64_t useful = 0;
+  for (int64_t f = 0; f < F; ++f)
+    for (int64_t g = 0; g < F; ++g)
+      if (attends(f, g)) useful += T * T;
+  if (useful_pairs) *useful_pairs = useful;
+
+  const bool fill = q_tiles || kv_ptr || kv_iv || kv_flag;
+  if (fill && (!q_tiles || !kv_ptr || !kv_iv || !kv_flag))
+    return fail(ATTN_E_INVAL, "q_tiles, kv_ptr, kv_iv and kv_flag must be all NULL or all non-NULL");
+  const int64_t cap_qt = *n_qt, cap_nnz = *nnz;
+  int64_t t = 0, e = 0;
+  if (fill && cap_qt >= 1) kv_ptr[0] = 0;
+  for (int64_t qs = 0; qs < N; qs += block_q, ++t) {
+    const int64_t qe = std::min<int64_t>(qs + block_q, N);
+    bool empty = true;
+    int64_t run_s = -1, run_kind = 0;
+    auto close = [&](int64_t end) {
+      if (run_s < 0) return;
+      if (fill && e < cap_nnz) {
+        kv_iv[2 * e] = (int32_t)run_s;
+        kv_iv[2 * e + 1] = (int32_t)(end - run_s);
+        kv_flag[e] = run_kind == 2 ? 1 : 0;
+      }
+      ++e;
+      run_s = -1;
+    };
+    for (int64_t ks = 0; ks < N; ks += granule) {
+      const int64_t ke = std::min<int64_t>(ks + granule, N);
+      const int kind = block_kind(qs, qe, ks, ke);
+      if (kind == 0 || kind != run_kind) close(ks);
+      if (kind != 0) {
+        empty = false;
+        if (run_s < 0) { run_s = ks; run_kind = kind; }
+      }
+      run_kind = kind == 0 ? 0 : run_kind;
+    }
+    close(N);
+    if (empty) return fail(ATTN_E_PATTERN, "a query tile attends no key");
+    if (fill && t < cap_qt) {
+      q_tiles[2 * t] = (int32_t)qs;
+      q_tiles[2 * t + 1] = (int32_t)(qe - qs);
+      kv_ptr[t + 1] = (int32_t)e;
+    }
+    if (t > 2147483647LL / 2 || e > 2147483647LL / 2) return fail(ATTN_E_SIZE, "block list too large");
+  }
+  const bool short_cap = fill && (cap_qt < t || cap_nnz < e);
+  *n_qt = (int32_t)t;
+  *nnz = (int32_t)e;
+  if (short_cap) return fail(ATTN_E_SIZE, "output capacity too small");
+  return bsvf::ok();
+}
+
 int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int32_t* kv_iv,
                         int32_t n_qt, int32_t batch, int32_t heads, int32_t group,
                         int32_t num_xcd, int32_t* work_order, int32_t* n_work) {

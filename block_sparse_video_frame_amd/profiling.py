@@ -25,14 +25,17 @@ import csv
 import glob
 import json
 import os
+import re
 from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
-    if "fwd_bound_blocks" in kernel:
-        return "attn_fwd[bound]"
-    if "fwd_kernel" in kernel:
-        return "attn_fwd[bound]" if "true>" in kernel else "attn_fwd[online]"
+    m = re.search(r"fwd_kernel<([^>]*)>", kernel)
+    if m:
+        args = [x.strip() for x in m.group(1).split(",")]
+        path = "bound" if len(args) > 3 and args[3] == "true" else "online"
+        masked = len(args) > 4 and args[4] == "true"
+        return f"attn_fwd[{path}{',masked' if masked else ''}]"
     if "norms_kernel" in kernel:
         return "attn_norms"
     if "zero_head_max" in kernel:

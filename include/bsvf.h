@@ -118,6 +118,32 @@ int attn_build_blocks(const attn_pattern_t* p, int32_t block_q,
                       int64_t* useful_pairs, int32_t* n_qt, int32_t* nnz);
 
 /*
+ * attn_build_blocks_granular — host, integer only, deterministic.
+ * The block list of the frame-unaware layout, for comparison with the
+ * frame-aligned one (the layout the pages moved away from: fixed blocks
+ * whose edges ignore frame edges, so some blocks are partly masked; vatt-ghern
+ * section 把 block 縮到 16, bytechap "How it works", cloudcurated Wall 2).
+ *   q_tiles [n_qt][2]: tiles of block_q consecutive rows from token 0 (the last
+ *       one shorter when N % block_q != 0), regardless of frames.
+ *   kv_iv [nnz][2], kv_ptr: per tile, maximal ascending runs of key blocks of
+ *       `granule` consecutive keys (the last block of the sequence shorter)
+ *       that some (row, key) pair of the tile attends, split where the flag
+ *       changes;
+ *   kv_flag [nnz]: 1 when some pair of the run's blocks is masked (the kernel
+ *       then evaluates the frame mask per element), 0 when every pair is
+ *       attended.
+ *   *useful_pairs: as attn_build_blocks.
+ * granule must be a positive multiple of 64 (so every 64-key stage lies in
+ * one run), block_q a positive multiple of 16.  Same two-call protocol as
+ * attn_build_blocks (kv_flag joins the three arrays: all NULL or none).
+ * Errors: as attn_build_blocks; ATTN_E_ALIGN also for a bad granule.
+ */
+int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t block_q,
+                               int32_t* q_tiles, int32_t* kv_ptr, int32_t* kv_iv,
+                               int32_t* kv_flag, int64_t* useful_pairs, int32_t* n_qt,
+                               int32_t* nnz);
+
+/*
  * attn_build_schedule — host, integer only, deterministic.
  * Launch order for attn_fwd over batch*heads*n_qt work items (item
  * w = tile + n_qt * (head + heads * batch_index)).  A tile's cost is
@@ -215,6 +241,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const attn_blocks_t* blocks, const float* q_norm,
              const float* k_gmax, const float* head_max, int32_t softmax_mode,
              int32_t* head_path_out, hipStream_t stream);
+
+/*
+ * attn_fwd_masked — device; attn_fwd over the frame-unaware layout of
+ * attn_build_blocks_granular, for comparison with the frame-aligned kernel
+ * (the pages' point: blocks that ignore frame edges need a mask predicate on
+ * every partly attended block; vatt-ghern section 把 block 縮到 16, bytechap
+ * "How it works").  Same arguments, results and errors as attn_fwd, plus:
+ *   kv_flag  device int32 [blocks->nnz]: the flags from
+ *            attn_build_blocks_granular (1 = evaluate the frame mask per
+ *            score; 0 = every pair attended);
+ *   pattern  host: the frame pattern the list was built from (its
+ *            num_frames * tokens_per_frame must equal seq_len).
+ * The result is the same attention as attn_fwd on the aligned list, up to
+ * summation order.  Requires tokens_per_frame >= 64, global frames below 64,
+ * and a list built with a granule that is a multiple of 64 (each 64-key stage
+ * then lies in one run); ATTN_E_UNSUPPORTED / ATTN_E_PATTERN otherwise.
+ */
+int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                    float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+                    int32_t head_dim, const int64_t* strides, float scale,
+                    const attn_blocks_t* blocks, const int32_t* kv_flag,
+                    const attn_pattern_t* pattern, const float* q_norm, const float* k_gmax,
+                    const float* head_max, int32_t softmax_mode, int32_t* head_path_out,
+                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

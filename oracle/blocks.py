@@ -87,6 +87,55 @@ def derive_blocks(pattern, block_q, check_rows="ends"):
     }
 
 
+def derive_blocks_granular(pattern, granule, block_q, check_rows="frames"):
+    """Block list of the frame-unaware layout: query tiles of ``block_q``
+    consecutive rows and key blocks of ``granule`` consecutive keys over the
+    whole sequence, with no regard to frame edges (the layout the pages moved
+    away from; vatt-ghern section 把 block 縮到 16, bytechap "How it works").
+
+    A key block is kept when some (row, key) pair of the tile attends it and
+    is flagged partial (1) unless every pair does.  Intervals are maximal runs
+    of kept blocks with equal flags, ascending.  ``useful_pairs`` is the same
+    count as for the aligned layout (the mask does not change).
+
+    ``check_rows="all"`` evaluates the dense mask for every row of a tile;
+    ``"frames"`` evaluates one row per frame present in the tile (rows of one
+    frame have identical mask rows by the mask's definition).
+    """
+    T = pattern.tokens_per_frame
+    N = pattern.num_frames * T
+    if granule <= 0 or granule % 64 or block_q <= 0 or block_q % 16 or T % 16:
+        raise ValueError("granule must be a multiple of 64, block_q and T multiples of 16")
+    q_tiles, kv_ptr, kv_iv, kv_flag = [], [0], [], []
+    for qs in range(0, N, block_q):
+        qe = min(qs + block_q, N)
+        if check_rows == "all":
+            rows = np.arange(qs, qe)
+        else:
+            rows = np.unique(np.clip(np.arange(qs // T, (qe - 1) // T + 1) * T, qs, qe - 1))
+        M = frame_mask(pattern, rows, N)
+        if not M.any():
+            raise ValueError("a query tile attends no key")
+        run = None  # [start, flag]
+        for ks in range(0, N, granule):
+            ke = min(ks + granule, N)
+            sub = M[:, ks:ke]
+            kind = 0 if not sub.any() else (1 if sub.all() else 2)
+            if run is not None and (kind == 0 or kind != run[1]):
+                kv_iv.append((run[0], ks - run[0]))
+                kv_flag.append(1 if run[1] == 2 else 0)
+                run = None
+            if kind and run is None:
+                run = [ks, kind]
+        if run is not None:
+            kv_iv.append((run[0], N - run[0]))
+            kv_flag.append(1 if run[1] == 2 else 0)
+        q_tiles.append((qs, qe - qs))
+        kv_ptr.append(len(kv_iv))
+    return {"q_tiles": q_tiles, "kv_ptr": kv_ptr, "kv_iv": kv_iv, "kv_flag": kv_flag,
+            "n_qt": len(q_tiles), "nnz": len(kv_iv)}
+
+
 def frame_pairs(pattern):
     """Number of (query frame, key frame) pairs the mask allows."""
     T = pattern.tokens_per_frame

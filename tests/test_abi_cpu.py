@@ -248,3 +248,66 @@ def test_norms_validation(over, status):
     s = (ctypes.c_int64 * 3)(a["N"] * a["D"] * 2, a["N"] * a["D"], a["D"])
     st = L.attn_norms(a["q"], a["k"], a["B"], a["H"], a["N"], a["D"], s, s, a["qn"], a["kg"], a["hm"], None)
     assert st == status
+
+
+# ---- frame-unaware layout (alignment ablation) -------------------------------------------
+
+
+def _granular_lists(blk):
+    return ([tuple(x) for x in blk.q_tiles.tolist()], blk.kv_ptr.tolist(),
+            [tuple(x) for x in blk.kv_iv.tolist()], blk.kv_flag.tolist())
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if n != "stress"])
+@pytest.mark.parametrize("granule", [64, 128])
+def test_granular_builder_matches_oracle_on_workloads(name, granule):
+    p = WORKLOADS[name].pattern
+    got = bs.build_blocks_granular(p, granule, 256)
+    want = BL.derive_blocks_granular(p, granule, 256)
+    qt, kp, kv, fl = _granular_lists(got)
+    assert qt == want["q_tiles"] and kp == want["kv_ptr"] and kv == want["kv_iv"] and fl == want["kv_flag"]
+    assert got.useful_pairs == BL.derive_blocks(p, 256)["useful_pairs"]
+
+
+def test_granular_builder_matches_oracle_on_random_patterns():
+    rnd = random.Random(23)
+    for _ in range(60):
+        F = rnd.randint(1, 9)
+        T = 16 * rnd.randint(4, 24)
+        gl = tuple(sorted(set(rnd.randint(0, F - 1) for _ in range(rnd.randint(0, 2)))))
+        p = Pattern(F, T, rnd.randint(0, 2), rnd.randint(0, 2), gl)
+        granule = rnd.choice([64, 128, 192])
+        bq = 16 * rnd.randint(1, 16)
+        got = bs.build_blocks_granular(p, granule, bq)
+        want = BL.derive_blocks_granular(p, granule, bq, check_rows="all")
+        qt, kp, kv, fl = _granular_lists(got)
+        assert qt == want["q_tiles"] and kp == want["kv_ptr"] and kv == want["kv_iv"] and fl == want["kv_flag"], p
+
+
+def test_granular_layout_covers_the_mask_exactly():
+    """Runs flagged 0 are fully attended by every row of the tile, and the union
+    of a tile's runs contains every attended key of every row."""
+    from oracle.attention import frame_mask
+    p = Pattern(6, 160, 1, 1, (0,))
+    blk = bs.build_blocks_granular(p, 128, 128)
+    N = p.num_frames * p.tokens_per_frame
+    for t in range(blk.n_qt):
+        qs, nr = blk.q_tiles[t]
+        M = frame_mask(p, np.arange(qs, qs + nr), N)
+        cover = np.zeros(N, bool)
+        for e in range(blk.kv_ptr[t], blk.kv_ptr[t + 1]):
+            ks, kl = blk.kv_iv[e]
+            cover[ks:ks + kl] = True
+            if blk.kv_flag[e] == 0:
+                assert M[:, ks:ks + kl].all()
+            else:
+                assert not M[:, ks:ks + kl].all()
+        assert not (M & ~cover[None, :]).any()
+
+
+def test_granular_builder_errors():
+    p = Pattern(3, 64, 1, 1)
+    with pytest.raises(bs.AttnError):
+        bs.build_blocks_granular(p, 96, 128)      # granule not a multiple of 64
+    with pytest.raises(bs.AttnError):
+        bs.build_blocks_granular(p, 128, 40)      # block_q not a multiple of 16

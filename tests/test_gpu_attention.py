@@ -195,3 +195,49 @@ def test_errors_with_device_tensors():
     with pytest.raises(bs.AttnError) as e:
         bs.attention(bad, bad, bad, blk, 0.125, 0)
     assert e.value.status == 5
+
+
+# ---- frame-unaware layout: fixed blocks with a per-element frame mask ---------------------
+
+GRANULAR = [c for c in range(len(SMALL)) if SMALL[c][0].tokens_per_frame >= 64]
+
+
+@pytest.mark.parametrize("case", GRANULAR)
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("granule,bq", [(128, 256), (64, 128)])
+def test_granular_small_all_rows(case, mode, granule, bq):
+    p, B, H, D, _ = SMALL[case]
+    q, k, v = random_qkv(B, H, p.seq_len, D, seed=200 + case)
+    scale = 1.0 / math.sqrt(D)
+    res = run_gpu(q, k, v, p, scale, mode, block_q=bq, granule=granule)
+    O, L = OA.attention(q, k, v, p, scale)
+    e = errors(res["o"], res["lse"], O, L)
+    assert within(e), e
+    assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
+
+
+@pytest.mark.parametrize("name", ["720p", "sr"])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_granular_workload_sampled_rows(name, mode):
+    wl = WORKLOADS[name]
+    q, k, v = inputs(name)
+    rows = rows_for(name)
+    res = run_gpu(q, k, v, wl.pattern, wl.scale, mode, granule=128)
+    O, L = oracle_rows(name, rows)
+    e = errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L)
+    print(name, mode, e)
+    assert within(e), e
+    assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
+
+
+def test_granular_agrees_with_aligned():
+    """Both layouts compute the same attention: outputs within the band of each
+    other, and the same head paths."""
+    p, B, H, D, _ = SMALL[6]
+    q, k, v = random_qkv(B, H, p.seq_len, D, seed=77)
+    scale = 1.0 / math.sqrt(D)
+    a = run_gpu(q, k, v, p, scale, 1)
+    g = run_gpu(q, k, v, p, scale, 1, granule=128)
+    e = errors(g["o"], g["lse"], a["o"], a["lse"])
+    assert within(e), e
+    assert (a["head_path"] == g["head_path"]).all()
