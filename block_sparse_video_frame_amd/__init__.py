@@ -23,12 +23,12 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "PATH_ONLINE", "PATH_BOUND",
+    "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "PATH_ONLINE", "PATH_BOUND",
     "MAX_BLOCK_Q", "ELIGIBLE_NATS", "AttnError", "lib", "library_path", "abi_version",
     "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "attention",
 ]
 
-SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED = 0, 1, 2
+SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE = 0, 1, 2, 3
 PATH_ONLINE, PATH_BOUND = 0, 1
 MAX_BLOCK_Q = 256
 ELIGIBLE_NATS = 60.0

@@ -774,7 +774,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   e0 = max(0, min(e0, a.nnz));
   e1 = max(e0, min(e1, a.nnz));
 
-  // Head path: uniform per workgroup.
+  // Softmax path: uniform per workgroup; per head (modes 1, 2) or per tile
+  // (mode 3, which needs the tile's largest query and key norms first).
+  const bool per_tile = a.mode == ATTN_SOFTMAX_BOUND_TILE;
   bool bound = false;
   if (a.mode == ATTN_SOFTMAX_BOUND_FORCED) {
     bound = true;
@@ -782,29 +784,37 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
     bound = 2.0f * a.scale * mq * mk <= ATTN_ELIGIBLE_NATS;
   }
-  if (bound != BOUND) return;
-  if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = bound ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
+  if (!per_tile && bound != BOUND) return;
 
-  // Tile-wide max key norm over every attended 16-key granule (bound only).
-  float kfac = 0.0f;
-  if constexpr (BOUND) {
-    float km = 0.0f;
+  // Tile-wide max key norm over every attended 16-key granule.
+  float km = 0.0f;
+  if (BOUND || per_tile) {
+    float* red = reinterpret_cast<float*>(smem + C::STAGE);
     const float* kg = k_gmax + (int64_t)bh * (a.N / 16);
     for (int e = e0; e < e1; ++e) {
       const int ks = kv_iv[2 * e], kl = kv_iv[2 * e + 1];
       if (!interval_ok(ks, kl, a.N)) continue;
       for (int g = ks / 16 + tid; g < (ks + kl) / 16; g += C::NT) km = fmaxf(km, kg[g]);
     }
+    float qm = 0.0f;
+    if (per_tile)
+      for (int r = tid; r < nr; r += C::NT) qm = fmaxf(qm, a.q_norm[(int64_t)bh * a.N + qs + r]);
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) km = fmaxf(km, __shfl_xor(km, m));
-    float* red = reinterpret_cast<float*>(smem + C::STAGE);
-    if (lane == 0) red[wave] = km;
+    for (int m = 32; m >= 1; m >>= 1) {
+      km = fmaxf(km, __shfl_xor(km, m));
+      qm = fmaxf(qm, __shfl_xor(qm, m));
+    }
+    if (lane == 0) { red[wave] = km; red[NW + wave] = qm; }
     __syncthreads();
     km = red[0];
+    qm = red[NW];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) km = fmaxf(km, red[i]);
-    kfac = a.scale * km * kBoundMargin;
+    for (int i = 1; i < NW; ++i) { km = fmaxf(km, red[i]); qm = fmaxf(qm, red[NW + i]); }
+    if (per_tile) bound = 2.0f * a.scale * qm * km <= ATTN_ELIGIBLE_NATS;
   }
+  if (bound != BOUND) return;
+  if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = bound ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
+  const float kfac = BOUND ? a.scale * km * kBoundMargin : 0.0f;
 
   Tile<D, NQB, NW, BOUND> T;
   T.n = lane & 31;
@@ -914,7 +924,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (seq_len % 16) return fail(ATTN_E_ALIGN, "seq_len must be a multiple of 16");
   if (!strides) return fail(ATTN_E_INVAL, "strides is NULL");
   if (!(scale > 0.0f) || !(scale < 3.0e38f)) return fail(ATTN_E_INVAL, "scale must be positive and finite");
-  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_FORCED)
+  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_TILE)
     return fail(ATTN_E_INVAL, "bad softmax_mode");
   int st;
   if ((st = check_tensor("q", q, strides + 0, batch, heads, seq_len, head_dim))) return st;

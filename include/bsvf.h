@@ -65,8 +65,13 @@ enum {
   ATTN_SOFTMAX_ONLINE = 0,       /* running max with rescaling, every head */
   ATTN_SOFTMAX_BOUND = 1,        /* Cauchy-Schwarz shift on eligible heads,
                                     online fallback on the rest (the method) */
-  ATTN_SOFTMAX_BOUND_FORCED = 2  /* bound on every head (diagnostic only: may
+  ATTN_SOFTMAX_BOUND_FORCED = 2, /* bound on every head (diagnostic only: may
                                     underflow to l = 0 on loose heads) */
+  ATTN_SOFTMAX_BOUND_TILE = 3    /* the eligibility test per query tile instead
+                                    of per head: a tile takes the bound when
+                                    2 * scale * max|q| over its rows * max|k|
+                                    over its attended keys <= ATTN_ELIGIBLE_NATS,
+                                    else the running max */
 };
 
 /* Values written to head_path_out. */
@@ -228,7 +233,8 @@ typedef struct attn_blocks_t {
  *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-8);
  *       the factor keeps it above every score the kernel computes (the bound
  *       path multiplies Q by scale*log2(e) and rounds it to bf16 once).
- *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head.
+ *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head
+ *       (for ATTN_SOFTMAX_BOUND_TILE: the path of the head's first tile).
  * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,
  * bad mode, bad scale), ATTN_E_ALIGN (N % 16, block_q % 16, misaligned pointer
  * or stride), ATTN_E_UNSUPPORTED (D not 64/128, block_q > ATTN_MAX_BLOCK_Q,

@@ -71,3 +71,22 @@ def slack_bound(hmax, scale):
 def eligible(hmax, scale, limit=ELIGIBLE_NATS):
     """Per-head eligibility for the bound softmax, ``[B, H]`` bool (inclusive)."""
     return slack_bound(hmax, scale) <= limit
+
+
+def tile_slack_bound(q, k, pattern, scale, tiles):
+    """Per query tile, ``2 scale max_{rows of the tile} |q| max_{keys the tile
+    attends} |k|`` (nats), ``[B, H, n_tiles]``: the head-wide slack bound
+    restricted to one tile's rows and keys (finer-grained eligibility; the
+    pages check the bound per head, vatt-ghern section 拿掉 softmax 的序列相依).
+    ``tiles`` is a sequence of ``(first row, rows)``; a tile's keys are the keys
+    any of its rows attends (read from the dense mask)."""
+    qn = row_norms(q)
+    kn = row_norms(k)
+    B, H, N = qn.shape
+    out = np.empty((B, H, len(tiles)))
+    for t, (qs, nr) in enumerate(tiles):
+        keys = frame_mask(pattern, np.arange(qs, qs + nr), N).any(axis=0)
+        for b in range(B):
+            for h in range(H):
+                out[b, h, t] = 2.0 * scale * qn[b, h, qs:qs + nr].max() * kn[b, h, keys].max()
+    return out

@@ -105,21 +105,26 @@ def _draw(rng, shape):
     return rng.standard_normal(size=shape, dtype=np.float32)
 
 
-def random_qkv(batch, heads, seq_len, head_dim, seed=0, stress=False):
-    """Seeded bf16 Q, K, V (uint16 bit arrays, ``[B, H, N, D]``)."""
+def random_qkv(batch, heads, seq_len, head_dim, seed=0, stress=False, stress_params=(0.75, 0.01, 8.0)):
+    """Seeded bf16 Q, K, V (uint16 bit arrays, ``[B, H, N, D]``).
+
+    ``stress``: every Q and K row is scaled by exp(sigma * z), z ~ N(0, 1)
+    independently per row, and a fraction ``rate`` of the K rows (independent
+    uniforms) by ``scale`` more; ``stress_params = (sigma, rate, scale)``."""
     rng = np.random.default_rng(seed)
     shape = (batch, heads, seq_len, head_dim)
     q = _draw(rng, shape)
     k = _draw(rng, shape)
     v = _draw(rng, shape)
     if stress:
+        sigma, rate, scale = (np.float32(x) for x in stress_params)
         rows = (batch, heads, seq_len)
         zq = _draw(rng, rows)
         zk = _draw(rng, rows)
         u = rng.random(size=rows, dtype=np.float32)
-        q *= np.exp(np.float32(0.75) * zq)[..., None]
-        ks = np.exp(np.float32(0.75) * zk)
-        ks = np.where(u < np.float32(0.01), ks * np.float32(8.0), ks).astype(np.float32)
+        q *= np.exp(sigma * zq)[..., None]
+        ks = np.exp(sigma * zk)
+        ks = np.where(u < rate, ks * scale, ks).astype(np.float32)
         k *= ks[..., None]
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
 

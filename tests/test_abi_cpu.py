@@ -217,7 +217,8 @@ def fwd_call(**over):
     (dict(blocks=None), 1),
     (dict(strides=None), 1),
     (dict(B=0), 1),
-    (dict(mode=3), 1),
+    (dict(mode=4), 1),                     # no such mode
+    (dict(mode=3), 5),                     # per-tile bound without norms
     (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1),
     (dict(D=96), 5),

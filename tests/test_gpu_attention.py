@@ -241,3 +241,71 @@ def test_granular_agrees_with_aligned():
     e = errors(g["o"], g["lse"], a["o"], a["lse"])
     assert within(e), e
     assert (a["head_path"] == g["head_path"]).all()
+
+
+# ---- per-tile eligibility (mode 3) --------------------------------------------------------
+
+
+def _frame_scaled_inputs(p, B, H, D, frame, factor, seed):
+    """N(0,1) bf16 inputs whose Q and K rows in one frame are scaled by
+    `factor` (rounded to bf16 once): heads that are ineligible as a whole,
+    with benign tiles away from that frame."""
+    from synth import f32_to_bf16_bits
+    q, k, v = random_qkv(B, H, p.seq_len, D, seed=seed)
+    T = p.tokens_per_frame
+    out = []
+    for x in (q, k):
+        f = OA.widen(x).astype(np.float32)
+        f[:, :, frame * T:(frame + 1) * T] *= np.float32(factor)
+        out.append(f32_to_bf16_bits(f))
+    return out[0], out[1], v
+
+
+def test_tile_eligibility_keeps_the_bound_on_benign_tiles():
+    p = Pattern(6, 160, 1, 1)
+    B, H, D = 1, 2, 128
+    q, k, v = _frame_scaled_inputs(p, B, H, D, frame=4, factor=3.0, seed=31)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    O, L = OA.attention(q, k, v, p, scale)
+    head = ON.slack_bound(ON.head_max(ON.row_norms(q), ON.row_norms(k)), scale)
+    assert (head > ON.ELIGIBLE_NATS).all()                      # mode 1: every head online
+    r1 = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND)
+    assert (r1["head_path"] == bs.PATH_ONLINE).all()
+    r3 = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND_TILE)
+    # Frame 4's rows attend sharply, so |O| reaches about 3 there; bf16's
+    # half-ulp alone is then ~0.008.  The absolute bound of the workloads
+    # (whose |O| stays below 1) is scaled by max(1, |O_ref|) per element.
+    s = np.maximum(1.0, np.abs(O))
+    for r in (r1, r3):
+        e = errors(r["o"] / s, r["lse"], O / s, L)
+        assert within(e), e
+    blk = bs.build_blocks_for(p, 256)
+    tiles = [tuple(map(int, t)) for t in blk.q_tiles]
+    tb = ON.tile_slack_bound(q, k, p, scale, tiles)
+    elig = tb <= ON.ELIGIBLE_NATS
+    # keep a margin from the threshold so fp32 and fp64 agree on every decision
+    assert (np.abs(tb - ON.ELIGIBLE_NATS) > 1e-3 * ON.ELIGIBLE_NATS).all()
+    assert elig.any() and (~elig).any()
+    mx = OA.scores_max(q, k, p, scale)
+    bd = ON.row_bound(q, k, p, scale)
+    for t, (qs, nr) in enumerate(tiles):
+        sl = slice(qs, qs + nr)
+        for b in range(B):
+            for h in range(H):
+                shift = r3["shift"][b, h, sl]
+                if elig[b, h, t]:   # bound: the tile's fixed Cauchy-Schwarz shift
+                    assert (shift >= mx[b, h, sl]).all()
+                    assert (np.abs(shift - bd[b, h, sl] * (1 + 2.0 ** -8)) <= 1e-5 * np.maximum(bd[b, h, sl], 1)).all()
+                else:               # online: the running max ends at the row max
+                    assert (np.abs(shift - mx[b, h, sl]) <= 1e-3 * np.maximum(np.abs(mx[b, h, sl]), 1)).all()
+
+
+@pytest.mark.parametrize("name", ["720p", "stress"])
+def test_tile_eligibility_workloads(name):
+    wl = WORKLOADS[name]
+    q, k, v = inputs(name)
+    rows = rows_for(name)
+    res = run_gpu(q, k, v, wl.pattern, wl.scale, bs.SOFTMAX_BOUND_TILE)
+    O, L = oracle_rows(name, rows)
+    e = errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L)
+    assert within(e), e

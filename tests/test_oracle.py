@@ -203,3 +203,26 @@ def test_eligibility_on_workload_heads():
             assert (sl < 40.0).all()
         else:
             assert (sl > 1000.0).all()
+
+
+def test_tile_slack_bound_pins():
+    """The per-tile slack bound: by explicit loops on a tiny case, never above the
+    head-wide bound, and equal to it when one tile covers every row."""
+    p = Pattern(3, 32, 1, 0)
+    q, k, _ = random_qkv(1, 2, p.seq_len, 16, seed=4)
+    scale = 0.25
+    tiles = [(0, 32), (32, 32), (64, 32)]
+    got = NM.tile_slack_bound(q, k, p, scale, tiles)
+    qf, kf = A.widen(q), A.widen(k)
+    for h in range(2):
+        for t, (qs, nr) in enumerate(tiles):
+            f = qs // 32
+            key_frames = [g for g in range(3) if -1 <= g - f <= 0]
+            qmax = max(math.sqrt(sum(x * x for x in qf[0, h, r])) for r in range(qs, qs + nr))
+            kmax = max(math.sqrt(sum(x * x for x in kf[0, h, j])) for g in key_frames for j in range(32 * g, 32 * g + 32))
+            assert abs(got[0, h, t] - 2 * scale * qmax * kmax) <= 1e-12 * got[0, h, t]
+    head = NM.slack_bound(NM.head_max(NM.row_norms(q), NM.row_norms(k)), scale)
+    assert (got <= head[..., None] * (1 + 1e-15)).all()
+    whole = NM.tile_slack_bound(q, k, Pattern(3, 32, 2, 2), scale, [(0, 96)])
+    head2 = NM.slack_bound(NM.head_max(NM.row_norms(q), NM.row_norms(k)), scale)
+    assert np.allclose(whole[..., 0], head2, rtol=1e-14)
