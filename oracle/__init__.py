@@ -22,9 +22,12 @@ Modules
              boolean mask.
   norms      fp64 row norms, per-16-key maxima, per-head maxima, the per-row
              bound and the per-head eligibility test.
+  producer   the Q/K producer that emits the norms in its epilogue: per-head
+             RMS norm with a weight, rotary embedding of adjacent pairs, one
+             bf16 rounding (straight from fp64), norms of the written rows.
 
 Every function here is pinned by the ``-m "not gpu"`` tests in ``tests/`` to
 something other than itself (brute force, closed forms, a library routine or
 an invariant).  None is "parity unpinned".
 """
-from . import attention, blocks, norms  # noqa: F401
+from . import attention, blocks, norms, producer  # noqa: F401

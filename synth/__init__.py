@@ -24,6 +24,10 @@ Q, K, V first, then ``z_q``, ``z_k`` (``[B, H, N]`` standard normal) and an
 outlier uniform ``[B, H, N]``; each Q row is multiplied by ``exp(0.75 z_q)``,
 each K row by ``exp(0.75 z_k)`` and, where the uniform is below 0.01, by 8;
 all in float32, rounded to bf16 once at the end.  V is left unscaled.
+
+The Q/K producer (per-head RMS norm, then rotary embedding) takes the same
+Q and K as its pre-norm input, RMS-norm weights from ``norm_weights`` and
+rotary tables from ``rope_tables`` on the frame grids of ``FRAME_GRID``.
 """
 from __future__ import annotations
 
@@ -33,8 +37,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = [
-    "Pattern", "Workload", "WORKLOADS", "f32_to_bf16_bits", "bf16_bits_to_f32",
-    "make_qkv", "random_qkv", "sha256",
+    "Pattern", "Workload", "WORKLOADS", "FRAME_GRID", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "make_qkv", "random_qkv", "rope_tables", "norm_weights", "sha256",
 ]
 
 
@@ -78,6 +82,17 @@ WORKLOADS = {
     "1080p": Workload("1080p", 1, 8, 128, Pattern(7, 8160, 1, 1, (0,))),
     "stress": Workload("stress", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), stress=True),
     "sr": Workload("sr", 1, 16, 64, Pattern(5, 14400, 0, 0)),
+}
+
+
+# Latent grid (rows, columns) of one frame: tokens_per_frame = rows * columns,
+# token t of a frame sits at row t // columns, column t % columns.
+FRAME_GRID = {
+    "tiny": (6, 8),
+    "720p": (45, 80),
+    "1080p": (68, 120),
+    "stress": (45, 80),
+    "sr": (90, 160),
 }
 
 
@@ -137,3 +152,40 @@ def make_qkv(wl: Workload, seed: int | None = None):
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def rope_tables(pattern: Pattern, head_dim: int, grid, theta: float = 10000.0):
+    """Rotary angle tables ``cos, sin`` (float32 ``[N, D/2]``) for 3-D video
+    positions: token ``n`` of frame ``f = n // T`` at in-frame index ``t`` has
+    position ``(f, t // W, t % W)`` on a ``grid = (rows, W)`` latent grid.  The
+    ``D/2`` adjacent-element pairs are split into a frame group of
+    ``D/2 - 2 * (D/2 // 3)`` pairs and a row and a column group of ``D/2 // 3``
+    pairs each; pair ``j`` of a group of ``n_a`` pairs turns by
+    ``position * theta ** (-j / n_a)``.  Angles and their cos/sin are taken in
+    float64 and stored as float32."""
+    T, N = pattern.tokens_per_frame, pattern.seq_len
+    rows, W = grid
+    if rows * W != T:
+        raise ValueError("grid must cover the frame exactly")
+    half = head_dim // 2
+    n_hw = half // 3
+    groups = (half - 2 * n_hw, n_hw, n_hw)
+    n = np.arange(N, dtype=np.int64)
+    t = n % T
+    pos = (n // T, t // W, t % W)
+    ang = np.empty((N, half), dtype=np.float64)
+    col = 0
+    for p, na in zip(pos, groups):
+        freq = theta ** (-np.arange(na, dtype=np.float64) / na)
+        ang[:, col:col + na] = p[:, None].astype(np.float64) * freq[None, :]
+        col += na
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def norm_weights(head_dim: int, seed: int = 1, sigma: float = 0.25):
+    """RMS-norm weights for Q and K: float32 ``[D]`` each, ``exp(sigma * z)``
+    with ``z`` standard normal from ``default_rng(seed)`` (Q's first)."""
+    rng = np.random.default_rng(seed)
+    gq = np.exp(np.float32(sigma) * _draw(rng, (head_dim,))).astype(np.float32)
+    gk = np.exp(np.float32(sigma) * _draw(rng, (head_dim,))).astype(np.float32)
+    return gq, gk
