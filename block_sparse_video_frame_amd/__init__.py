@@ -25,7 +25,8 @@ import numpy as np
 __all__ = [
     "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "PATH_ONLINE", "PATH_BOUND",
     "MAX_BLOCK_Q", "ELIGIBLE_NATS", "AttnError", "lib", "library_path", "abi_version",
-    "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "attention",
+    "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "qk_prep",
+    "attention",
 ]
 
 SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE = 0, 1, 2, 3
@@ -104,6 +105,9 @@ def lib():
     L.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.c_float,
                            ctypes.POINTER(_Blocks), _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    L.attn_qk_prep.restype = ctypes.c_int
+    L.attn_qk_prep.argtypes = [_VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_int32, _I64P, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP]
     if L.attn_abi_version() != ABI_VERSION:
         raise RuntimeError("libbsvf.so ABI version mismatch; rebuild it")
     _LIB = L
@@ -271,6 +275,43 @@ def _norms(q, k, out=None):
 
 
 norms = _norms
+
+
+def qk_prep(q_in, k_in, q_gamma, k_gamma, rope_cos, rope_sin, eps: float = 1e-6, q_out=None, k_out=None,
+            norms: bool = True, norms_out=None):
+    """The Q/K producer (``attn_qk_prep``): per-head RMS norm with weights
+    ``q_gamma``/``k_gamma`` (fp32 ``[D]``), rotary embedding of adjacent pairs by
+    the fp32 ``[N, D/2]`` tables, bf16 out.  Returns ``(q_out, k_out, norms)``
+    where ``norms`` is the ``(q_norm, k_gmax, head_max)`` triple of the rows
+    written (as :func:`norms` would give), or None when ``norms`` is False.
+    Outputs default to new contiguous ``[B, H, N, D]`` tensors; passing
+    ``q_out=q_in`` (same strides) works in place."""
+    import torch
+    _check_qkv(q_in, k_in)
+    B, H, N, D = q_in.shape
+    if tuple(k_in.shape) != (B, H, N, D):
+        raise ValueError("q_in and k_in must have the same shape")
+    for name, t, shape in (("q_gamma", q_gamma, (D,)), ("k_gamma", k_gamma, (D,)),
+                           ("rope_cos", rope_cos, (N, D // 2)), ("rope_sin", rope_sin, (N, D // 2))):
+        if t.dtype != torch.float32 or t.device != q_in.device or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor on the inputs' device")
+    if q_out is None:
+        q_out = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=q_in.device)
+    if k_out is None:
+        k_out = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=q_in.device)
+    _check_qkv(q_out, k_out)
+    nm = None
+    if norms:
+        nm = norms_out if norms_out is not None else (
+            torch.empty(B, H, N, dtype=torch.float32, device=q_in.device),
+            torch.empty(B, H, N // 16, dtype=torch.float32, device=q_in.device),
+            torch.empty(B, H, 2, dtype=torch.float32, device=q_in.device))
+    st = (ctypes.c_int64 * 12)(*(_strides(q_in) + _strides(k_in) + _strides(q_out) + _strides(k_out)))
+    qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
+    _check(lib().attn_qk_prep(q_in.data_ptr(), k_in.data_ptr(), q_out.data_ptr(), k_out.data_ptr(), B, H, N, D,
+                              st, q_gamma.data_ptr(), k_gamma.data_ptr(), ctypes.c_float(eps),
+                              rope_cos.data_ptr(), rope_sin.data_ptr(), qn, kg, hm, _stream(q_in)))
+    return q_out, k_out, nm
 
 
 def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: int = SOFTMAX_BOUND,

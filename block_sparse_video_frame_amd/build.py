@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbsvf.so")
-SOURCES = ["bsvf_host.cpp", "attn_norms.hip", "attn_fwd.hip"]
+SOURCES = ["bsvf_host.cpp", "attn_norms.hip", "attn_qk_prep.hip", "attn_fwd.hip"]
 ARCH = os.environ.get("BSVF_ARCH", "gfx950")
 
 

@@ -272,6 +272,45 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
                     const float* head_max, int32_t softmax_mode, int32_t* head_path_out,
                     hipStream_t stream);
 
+/*
+ * attn_qk_prep — device, HBM-bound: the producer of Q and K with the norms of
+ * attn_norms in its epilogue.  The pages hand the attention kernel
+ * precomputed norms (vatt-ghern, section 拿掉 softmax 的序列相依) and fuse
+ * producer stages so that each writes what the next reads, in its layout
+ * (cloudcurated, layout contracts after Wall 3).  Per row x of one head
+ * (fp32 arithmetic, one rounding to bf16, nearest even):
+ *   y   = x * gamma / sqrt(mean_e x_e^2 + eps)              (QK RMS norm)
+ *   out_2i   = y_2i * cos[n][i] - y_2i+1 * sin[n][i]        (rotary pairs)
+ *   out_2i+1 = y_2i * sin[n][i] + y_2i+1 * cos[n][i]
+ * then, over the rounded rows just written: q_norm, k_gmax and head_max
+ * exactly as attn_norms defines them, so attn_fwd can take them directly.
+ *   q_in, k_in: device bf16 [B][H][N][D]; q_out, k_out: device bf16 outputs
+ *       (an output may be its own input with identical strides; q_out and
+ *       k_out must not alias each other or the other input; any other
+ *       overlap between outputs and inputs is undefined and not detected).
+ *   strides: host int64 [4][3], element strides {b, h, n} of q_in, k_in,
+ *       q_out, k_out (d-stride 1), so e.g. a [B][N][H][D] projection output
+ *       is read in place and written in the attention's [B][H][N][D].
+ *   q_gamma, k_gamma: device fp32 [D] RMS-norm weights (one per tensor,
+ *       shared by the heads).  eps: finite, >= 0.
+ *   rope_cos, rope_sin: device fp32 [N][D/2] contiguous; entry [n][i] turns
+ *       pair (2i, 2i+1) of token n (any 1-D or 3-D position scheme; the
+ *       identity is cos = 1, sin = 0).
+ *   q_norm, k_gmax, head_max: attn_norms' outputs (contiguous fp32), all
+ *       three or all NULL (then only Q and K are written).
+ * Pointers 16-byte aligned.  Caller owns every buffer; enqueued on `stream`.
+ * Errors: ATTN_E_INVAL (NULL, non-positive sizes, bad eps, forbidden
+ * aliasing, only some norm outputs), ATTN_E_ALIGN (N % 16, misaligned
+ * pointer or stride), ATTN_E_UNSUPPORTED (D not 64 or 128), ATTN_E_SIZE
+ * (B > 65535 or too many rows), ATTN_E_HIP (launch failed).  All checks run
+ * before any launch; on error nothing is written.
+ */
+int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                 int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                 const int64_t* strides, const float* q_gamma, const float* k_gamma,
+                 float eps, const float* rope_cos, const float* rope_sin,
+                 float* q_norm, float* k_gmax, float* head_max, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,22 +37,30 @@ from . import norms as _norms
 def round_bf16(x) -> np.ndarray:
     """fp64 -> bf16 bit patterns (uint16), round to nearest, ties to even, in
     one step (no intermediate float32, so no double rounding).  Finite inputs
-    only; results beyond the largest bf16 become +-inf."""
-    x = np.asarray(x, dtype=np.float64)
+    only; results beyond the largest bf16 become +-inf.
+
+    In the normal range the fp64 pattern is rounded to bf16's 7 stored
+    fraction bits (a carry out of the fraction moves to the next binade);
+    below 2^-126 bf16's quantum is fixed at 2^-133 and the value is rounded
+    to a multiple of it."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
     if not np.isfinite(x).all():
         raise ValueError("round_bf16 takes finite values")
-    sign = np.where(np.signbit(x), np.uint16(0x8000), np.uint16(0))
-    a = np.abs(x)
-    _, e = np.frexp(a)                 # a = m * 2^e, m in [0.5, 1)
-    # bf16 keeps 8 significant bits: quantum 2^(e-8); below the normal range
-    # (a < 2^-126, e <= -126) the quantum stays 2^-133
-    q = np.maximum(e - 8, -133)
-    r = np.ldexp(np.rint(np.ldexp(a, -q)), q)   # rint: ties to even
+    u = x.view(np.uint64)
+    drop = np.uint64(45)                           # 52 - 7 fraction bits go
+    lsb = (u >> drop) & np.uint64(1)
+    r = ((u + np.uint64((1 << 44) - 1) + lsb) >> drop) << drop
+    rv = r.view(np.float64)
+    small = np.abs(x) < 2.0 ** -126
+    if small.any():
+        rv = np.where(small, np.rint(x * 2.0 ** 133) * 2.0 ** -133, rv)   # rint: ties to even
+    big = np.abs(rv) >= 2.0 ** 128
     with np.errstate(over="ignore"):
-        r32 = r.astype(np.float32)     # exact below 2^128: r has <= 8 significant bits
+        r32 = np.where(big, 0.0, rv).astype(np.float32)   # exact: <= 8 significant bits
     bits = (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
-    bits = np.where(r >= 2.0 ** 128, np.uint16(0x7F80), bits)
-    return bits | sign
+    bits = np.where(big, np.uint16(0x7F80), bits)
+    sign = np.where(np.signbit(x), np.uint16(0x8000), np.uint16(0))
+    return (bits & np.uint16(0x7FFF)) | sign
 
 
 def rms_normalize(x, gamma, eps):
@@ -81,13 +89,24 @@ def qk_norm_rope(x, gamma, eps, cos, sin):
     return rotate_pairs(rms_normalize(x, gamma, eps), cos, sin)
 
 
-def qk_prep(q, k, q_gamma, k_gamma, eps, cos, sin):
+def qk_prep(q, k, q_gamma, k_gamma, eps, cos, sin, chunk=4096):
     """Q and K through the producer, rounded to bf16, plus their norms.
 
     Returns ``(q_out bits, k_out bits, q_norm [B,H,N], k_gmax [B,H,N/16],
-    head_max [B,H,2])``; the norms are fp64 over the rounded rows."""
-    qo = round_bf16(qk_norm_rope(q, q_gamma, eps, cos, sin))
-    ko = round_bf16(qk_norm_rope(k, k_gamma, eps, cos, sin))
-    qn = _norms.row_norms(qo)
-    kn = _norms.row_norms(ko)
+    head_max [B,H,2])``; the norms are fp64 over the rounded rows.  Rows are
+    independent, so they are taken ``chunk`` at a time (bounded memory)."""
+    q, k = np.asarray(q), np.asarray(k)
+    B, H, N, _ = q.shape
+    outs = []
+    for x, g in ((q, q_gamma), (k, k_gamma)):
+        o = np.empty(x.shape, dtype=np.uint16)
+        n = np.empty((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                for r0 in range(0, N, chunk):
+                    r1 = min(N, r0 + chunk)
+                    o[b, h, r0:r1] = round_bf16(qk_norm_rope(x[b, h, r0:r1], g, eps, cos[r0:r1], sin[r0:r1]))
+                    n[b, h, r0:r1] = _norms.row_norms(o[b, h, r0:r1])
+        outs.append((o, n))
+    (qo, qn), (ko, kn) = outs
     return qo, ko, qn, _norms.granule_max(kn), _norms.head_max(qn, kn)

@@ -251,6 +251,38 @@ def test_norms_validation(over, status):
     assert st == status
 
 
+def prep_call(**over):
+    L = bs.lib()
+    a = dict(qi=FAKE, ki=FAKE + 0x100000, qo=FAKE + 0x200000, ko=FAKE + 0x300000, B=1, H=2, N=192, D=64,
+             strides=[192 * 64 * 2, 192 * 64, 64] * 4, gq=FAKE, gk=FAKE, eps=1e-6, cos=FAKE, sin=FAKE,
+             qn=FAKE, kg=FAKE, hm=FAKE)
+    a.update(over)
+    st = (ctypes.c_int64 * 12)(*a["strides"]) if a["strides"] is not None else None
+    return L.attn_qk_prep(a["qi"], a["ki"], a["qo"], a["ko"], a["B"], a["H"], a["N"], a["D"], st, a["gq"],
+                          a["gk"], ctypes.c_float(a["eps"]), a["cos"], a["sin"], a["qn"], a["kg"], a["hm"], None)
+
+
+_S = [192 * 64 * 2, 192 * 64, 64]
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(qi=None), 1), (dict(ko=None), 1), (dict(strides=None), 1), (dict(B=0), 1), (dict(H=-1), 1),
+    (dict(D=96), 5), (dict(N=200), 2), (dict(qo=FAKE + 0x200008), 2),
+    (dict(strides=_S * 2 + [192 * 64 * 2, 192 * 64, 60] + _S), 2),
+    (dict(gq=None), 1), (dict(sin=None), 1), (dict(cos=FAKE + 4), 2), (dict(gk=FAKE + 8), 2),
+    (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1), (dict(eps=float("inf")), 1),
+    (dict(kg=None), 1), (dict(qn=None, hm=None), 1),                     # some norm outputs only
+    (dict(qo=FAKE + 0x300000), 1),                                       # q_out == k_out
+    (dict(qo=FAKE + 0x100000), 1),                                       # q_out == k_in
+    (dict(qo=FAKE, strides=_S * 2 + [192 * 64 * 2, 192 * 64, 128] + _S), 1),  # in place, other strides
+    (dict(B=70000, strides=_S * 4), 4),
+])
+def test_qk_prep_validation(over, status):
+    assert prep_call(**over) == status
+    assert bs.lib().attn_last_error().startswith(bs.lib().attn_status_str(status))
+
+
 # ---- frame-unaware layout (alignment ablation) -------------------------------------------
 
 
