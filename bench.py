@@ -39,15 +39,22 @@ def _code_only(text: str) -> bytes:
     return " ".join(text.split()).encode()
 
 
-def source_hash() -> str:
-    """Hash of the code (not the comments) of the kernels, the host library and
-    the header."""
+# The sources each kernel is built from (the public header's declarations are
+# not part of it): counters taken on a kernel stay valid while these are
+# unchanged.
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "bsvf_device.h", "bsvf_internal.h"],
+    "attn_qk_prep": ["attn_qk_prep.hip", "bsvf_device.h", "bsvf_internal.h"],
+}
+
+
+def source_hash(kernel: str = "attn_fwd") -> str:
+    """Hash of the code (not the comments) of one kernel's sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_video_frame_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))] + [os.path.join(ROOT, "include", "bsvf.h")]
-    for path in files:
-        with open(path, encoding="utf-8") as fh:
-            h.update(os.path.basename(path).encode() + _code_only(fh.read()))
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(name.encode() + _code_only(fh.read()))
     return h.hexdigest()[:16]
 
 
@@ -63,6 +70,68 @@ def load_traffic(workload: str, mode: int):
     if d.get("source_hash") != source_hash() or int(d.get("mode", -1)) != mode:
         return None
     return d.get("bytes_per_launch")
+
+
+def load_producer_traffic(workload: str):
+    """HBM bytes per attn_qk_prep launch (with norms) from committed counter
+    runs on the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_qk_prep_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return d.get("bytes_per_launch") if d.get("source_hash") == source_hash("attn_qk_prep") else None
+
+
+def time_producer(bs, wl, q, k, dev, steps: int, warmup: int):
+    """attn_qk_prep with the norms in its epilogue, against the same producer
+    without them followed by attn_norms over its output (the unfused order).
+    Pre-norm Q and K are the workload's seeded tensors; weights and rotary
+    tables come from the seeded generators.  Outputs go to separate buffers."""
+    import torch
+    from synth import FRAME_GRID, norm_weights, rope_tables
+    B, H, N, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
+    gq, gk = (torch.from_numpy(x).to(dev) for x in norm_weights(D))
+    cos, sin = (torch.from_numpy(x).to(dev) for x in rope_tables(wl.pattern, D, FRAME_GRID[wl.name]))
+    qo, ko = torch.empty_like(q), torch.empty_like(k)
+    nm = (torch.empty(B, H, N, dtype=torch.float32, device=dev),
+          torch.empty(B, H, N // 16, dtype=torch.float32, device=dev),
+          torch.empty(B, H, 2, dtype=torch.float32, device=dev))
+
+    def fused():
+        bs.qk_prep(q, k, gq, gk, cos, sin, 1e-6, q_out=qo, k_out=ko, norms_out=nm)
+
+    def plain():
+        bs.qk_prep(q, k, gq, gk, cos, sin, 1e-6, q_out=qo, k_out=ko, norms=False)
+
+    def norms():
+        bs.norms(qo, ko, out=nm)
+
+    for _ in range(warmup):
+        fused(); plain(); norms()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        e[0].record(); fused(); e[1].record(); plain(); e[2].record(); norms(); e[3].record()
+    torch.cuda.synchronize()
+    t_fused = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_plain = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_norms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    # algorithmic bytes: Q, K read and written once, the rotary tables and
+    # weights read once, the norms written once
+    qk = 2 * B * H * N * D * 2
+    nbytes = 2 * qk + 2 * N * (D // 2) * 4 + 2 * D * 4 + 4 * B * H * (N + N // 16 + 2)
+    gbs = nbytes / (t_fused * 1e-3) / 1e9
+    print(f"[bench] attn_qk_prep {t_fused * 1e3:.1f} us with norms; {t_plain * 1e3:.1f} us without + "
+          f"attn_norms {t_norms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    return {"fused_us": round(t_fused * 1e3, 2), "plain_us": round(t_plain * 1e3, 2),
+            "attn_norms_us": round(t_norms * 1e3, 2), "unfused_us": round((t_plain + t_norms) * 1e3, 2),
+            "saved_us": round((t_plain + t_norms - t_fused) * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_producer_traffic(wl.name),
+                         "kernel": "attn_qk_prep", "per_launch_bytes": nbytes},
+            "source_hash": source_hash("attn_qk_prep")}
 
 
 def cpu_baseline(wl, q, k, v, target_s: float):
@@ -112,6 +181,9 @@ def main():
     ap.add_argument("--layout", default="aligned16", choices=["aligned16", "granular128"],
                     help="block layout: frame-aligned 16-token blocks (the method), or fixed 128-token "
                          "blocks that ignore frame edges with a per-element frame mask (ablation)")
+    ap.add_argument("--producer", action="store_true",
+                    help="also time attn_qk_prep (QK RMS norm + rotary, norms in its epilogue) against the "
+                         "same producer without norms followed by attn_norms")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for the byte counters)")
     args = ap.parse_args()
@@ -230,6 +302,8 @@ def main():
                      "per_launch_flop": useful_flop},
         "source_hash": source_hash(),
     }
+    if args.producer:
+        res["qk_prep"] = time_producer(bs, wl, q, k, dev, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, qb, kb, vb, args.cpu_seconds)

@@ -20,9 +20,10 @@
 //
 // HBM-bound.  A row of D bf16 is handled by D/8 consecutive lanes, 16 bytes
 // (8 elements, 4 rotary pairs) each, so the rotation needs no lane exchange
-// and one wave-wide access moves 1 KiB.  Workgroups are ordered head-fastest
-// so that the H workgroups reading the same rotary table rows run together.
-// Arithmetic is fp32 with one rounding to bf16.
+// and one wave-wide access moves 1 KiB.  A wave keeps the rotary table rows
+// of its granule in registers and walks the heads, so the tables (shared by
+// every head) are read from HBM once.  Arithmetic is fp32 with one rounding
+// to bf16.
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
@@ -31,8 +32,7 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 constexpr int kPrepWaves = kPrepThreads / 64;
-constexpr int kPrepGranulesPerWave = 2;
-constexpr int kPrepGranulesPerBlock = kPrepWaves * kPrepGranulesPerWave;
+constexpr int kPrepMaxHeads = 2048;  // per-head maxima live in LDS
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -47,7 +47,7 @@ struct PrepArgs {
   const float* cos;
   const float* sin;
   float eps;
-  int32_t H, N, chunks;
+  int32_t H, N;
   float* q_norm;
   float* k_gmax;
   float* head_max;
@@ -91,86 +91,109 @@ __device__ __forceinline__ u32x4 prep_chunk(u32x4 w, const float (&g)[8], f32x4 
   return out;
 }
 
+// A workgroup covers kPrepWaves consecutive 16-row granules of one batch
+// entry, one per wave, for every head.  A wave loads the rotary table rows of
+// its granule once, keeps them in registers and walks the heads.
 template <int D, bool NORMS>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   constexpr int LPR = D / 8;     // lanes per row
   constexpr int RPI = 64 / LPR;  // rows per wave-wide access
   constexpr int IPG = 16 / RPI;  // accesses per 16-row granule
+  extern __shared__ float hmax_lds[];  // [H][kPrepWaves][2] per-wave maxima
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x % a.H, chunk = blockIdx.x / a.H, b = blockIdx.y;
-  const int bh = b * a.H + h;
+  const int b = blockIdx.y;
   const int G = a.N / 16;
+  const int g = blockIdx.x * kPrepWaves + wave;
   const int c = lane % LPR, rsub = lane / LPR;
   const float inv_d = 1.0f / D;
 
-  float gq[8], gk[8];
-  {
-    const f32x4 q0 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c);
-    const f32x4 q1 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c + 4);
-    const f32x4 k0 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c);
-    const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { gq[e] = q0[e]; gq[4 + e] = q1[e]; gk[e] = k0[e]; gk[4 + e] = k1[e]; }
+  if constexpr (NORMS) {
+    for (int i = threadIdx.x; i < a.H * kPrepWaves * 2; i += kPrepThreads) hmax_lds[i] = 0.0f;
+    __syncthreads();
   }
-  const u16* qi = a.qi + b * a.s[0][0] + h * a.s[0][1];
-  const u16* ki = a.ki + b * a.s[1][0] + h * a.s[1][1];
-  u16* qo = a.qo + b * a.s[2][0] + h * a.s[2][1];
-  u16* ko = a.ko + b * a.s[3][0] + h * a.s[3][1];
-
-  float qmax = 0.0f, kmax = 0.0f;
-#pragma unroll 1
-  for (int gi = 0; gi < kPrepGranulesPerWave; ++gi) {
-    // the waves of a workgroup take neighbouring granules at the same time
-    const int g = chunk * kPrepGranulesPerBlock + gi * kPrepWaves + wave;
-    if (g >= G) break;
-    u32x4 qv[IPG], kv[IPG];
+  if (g < G) {
+    float gq[8], gk[8];
+    {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c + 4);
+      const f32x4 k0 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c);
+      const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { gq[e] = q0[e]; gq[4 + e] = q1[e]; gk[e] = k0[e]; gk[4 + e] = k1[e]; }
+    }
     f32x4 cv[IPG], sv[IPG];
 #pragma unroll
     for (int it = 0; it < IPG; ++it) {
       const int row = g * 16 + it * RPI + rsub;
-      qv[it] = *reinterpret_cast<const u32x4*>(qi + (int64_t)row * a.s[0][2] + 8 * c);
-      kv[it] = *reinterpret_cast<const u32x4*>(ki + (int64_t)row * a.s[1][2] + 8 * c);
       cv[it] = *reinterpret_cast<const f32x4*>(a.cos + (int64_t)row * (D / 2) + 4 * c);
       sv[it] = *reinterpret_cast<const f32x4*>(a.sin + (int64_t)row * (D / 2) + 4 * c);
     }
-    float kg = 0.0f;
+    auto load = [&](int h, u32x4 (&qv)[IPG], u32x4 (&kv)[IPG]) {
+      const u16* qi = a.qi + b * a.s[0][0] + h * a.s[0][1];
+      const u16* ki = a.ki + b * a.s[1][0] + h * a.s[1][1];
 #pragma unroll
-    for (int it = 0; it < IPG; ++it) {
-      const int row = g * 16 + it * RPI + rsub;
-      float sq, sk;
-      const u32x4 qr = prep_chunk<LPR>(qv[it], gq, cv[it], sv[it], a.eps, inv_d, sq);
-      const u32x4 kr = prep_chunk<LPR>(kv[it], gk, cv[it], sv[it], a.eps, inv_d, sk);
-      *reinterpret_cast<u32x4*>(qo + (int64_t)row * a.s[2][2] + 8 * c) = qr;
-      *reinterpret_cast<u32x4*>(ko + (int64_t)row * a.s[3][2] + 8 * c) = kr;
+      for (int it = 0; it < IPG; ++it) {
+        const int row = g * 16 + it * RPI + rsub;
+        qv[it] = *reinterpret_cast<const u32x4*>(qi + (int64_t)row * a.s[0][2] + 8 * c);
+        kv[it] = *reinterpret_cast<const u32x4*>(ki + (int64_t)row * a.s[1][2] + 8 * c);
+      }
+    };
+    auto work = [&](int h, const u32x4 (&qv)[IPG], const u32x4 (&kv)[IPG]) {
+      u16* qo = a.qo + b * a.s[2][0] + h * a.s[2][1];
+      u16* ko = a.ko + b * a.s[3][0] + h * a.s[3][1];
+      const int64_t bh = (int64_t)b * a.H + h;
+      float qm = 0.0f, kg = 0.0f;
+#pragma unroll
+      for (int it = 0; it < IPG; ++it) {
+        const int row = g * 16 + it * RPI + rsub;
+        float sq, sk;
+        const u32x4 qr = prep_chunk<LPR>(qv[it], gq, cv[it], sv[it], a.eps, inv_d, sq);
+        const u32x4 kr = prep_chunk<LPR>(kv[it], gk, cv[it], sv[it], a.eps, inv_d, sk);
+        *reinterpret_cast<u32x4*>(qo + (int64_t)row * a.s[2][2] + 8 * c) = qr;
+        *reinterpret_cast<u32x4*>(ko + (int64_t)row * a.s[3][2] + 8 * c) = kr;
+        if constexpr (NORMS) {
+#pragma unroll
+          for (int m = LPR / 2; m >= 1; m >>= 1) {
+            sq += __shfl_xor(sq, m);
+            sk += __shfl_xor(sk, m);
+          }
+          const float qn = __builtin_sqrtf(sq), kn = __builtin_sqrtf(sk);
+          if (c == 0) a.q_norm[bh * a.N + row] = qn;
+          qm = fmaxf(qm, qn);
+          kg = fmaxf(kg, kn);
+        }
+      }
       if constexpr (NORMS) {
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) {
-          sq += __shfl_xor(sq, m);
-          sk += __shfl_xor(sk, m);
+        for (int m = LPR; m < 64; m <<= 1) {
+          qm = fmaxf(qm, __shfl_xor(qm, m));
+          kg = fmaxf(kg, __shfl_xor(kg, m));
         }
-        const float qn = __builtin_sqrtf(sq), kn = __builtin_sqrtf(sk);
-        if (c == 0) a.q_norm[(int64_t)bh * a.N + row] = qn;
-        qmax = fmaxf(qmax, qn);
-        kg = fmaxf(kg, kn);
+        if (lane == 0) {
+          a.k_gmax[bh * G + g] = kg;
+          float* slot = hmax_lds + 2 * (h * kPrepWaves + wave);  // this wave's own slot
+          slot[0] = fmaxf(slot[0], qm);
+          slot[1] = fmaxf(slot[1], kg);
+        }
       }
-    }
-    if constexpr (NORMS) {
-#pragma unroll
-      for (int m = LPR; m < 64; m <<= 1) kg = fmaxf(kg, __shfl_xor(kg, m));
-      if (lane == 0) a.k_gmax[(int64_t)bh * G + g] = kg;
-      kmax = fmaxf(kmax, kg);
+    };
+#pragma unroll 1
+    for (int h = 0; h < a.H; ++h) {
+      u32x4 qv[IPG], kv[IPG];
+      load(h, qv, kv);
+      work(h, qv, kv);
     }
   }
   if constexpr (NORMS) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, m));
-    __shared__ float red[2][kPrepWaves];
-    if (lane == 0) { red[0][wave] = qmax; red[1][wave] = kmax; }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float mq = red[0][0], mk = red[1][0];
-      for (int w = 1; w < kPrepWaves; ++w) { mq = fmaxf(mq, red[0][w]); mk = fmaxf(mk, red[1][w]); }
-      // norms are >= 0, so the float order is the unsigned order of the bits
+    // norms are >= 0, so the float order is the unsigned order of the bits
+    for (int h = threadIdx.x; h < a.H; h += kPrepThreads) {
+      float mq = 0.0f, mk = 0.0f;
+      for (int w = 0; w < kPrepWaves; ++w) {
+        mq = fmaxf(mq, hmax_lds[2 * (h * kPrepWaves + w)]);
+        mk = fmaxf(mk, hmax_lds[2 * (h * kPrepWaves + w) + 1]);
+      }
+      const int64_t bh = (int64_t)b * a.H + h;
       atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh), __float_as_uint(mq));
       atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh + 1), __float_as_uint(mk));
     }
@@ -179,7 +202,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
 
 template <int D, bool NORMS>
 void prep_launch(const PrepArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prep_kernel<D, NORMS>), grid, dim3(kPrepThreads), 0, stream, a);
+  const size_t lds = NORMS ? sizeof(float) * 2 * kPrepWaves * a.H : 0;
+  hipLaunchKernelGGL((prep_kernel<D, NORMS>), grid, dim3(kPrepThreads), lds, stream, a);
 }
 
 bool same_strides(const int64_t* x, const int64_t* y) { return x[0] == y[0] && x[1] == y[1] && x[2] == y[2]; }
@@ -215,6 +239,7 @@ extern "C" int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, voi
   const int n_norm = (q_norm != nullptr) + (k_gmax != nullptr) + (head_max != nullptr);
   if (n_norm != 0 && n_norm != 3) return fail(ATTN_E_INVAL, "norm outputs must be all given or all NULL");
   if ((int64_t)batch > 65535) return fail(ATTN_E_SIZE, "batch exceeds 65535");
+  if (heads > kPrepMaxHeads) return fail(ATTN_E_SIZE, "heads exceeds 2048");
   if ((int64_t)batch * heads * seq_len > (int64_t)1 << 40) return fail(ATTN_E_SIZE, "too many rows");
 
   PrepArgs a;
@@ -232,13 +257,11 @@ extern "C" int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, voi
   a.H = heads;
   a.N = seq_len;
   const int granules = seq_len / 16;
-  a.chunks = (granules + kPrepGranulesPerBlock - 1) / kPrepGranulesPerBlock;
+  const int blocks = (granules + kPrepWaves - 1) / kPrepWaves;
   a.q_norm = q_norm;
   a.k_gmax = k_gmax;
   a.head_max = head_max;
-  if ((int64_t)a.chunks * heads > 0x7fffffff) return fail(ATTN_E_SIZE, "grid too large");
-
-  const dim3 grid(a.chunks * heads, batch);
+  const dim3 grid(blocks, batch);
   const bool norms = n_norm == 3;
   if (norms) {
     const int32_t hm_count = 2 * batch * heads;

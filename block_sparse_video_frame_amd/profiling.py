@@ -7,7 +7,8 @@ them into the short text/JSON summaries kept with the project:
   ``--kernel-trace --stats`` run (``*_kernel_stats.csv``);
 * ``counters``: per-kernel mean of each hardware counter per dispatch from a
   ``--pmc`` run (``*_counter_collection.csv``);
-* ``traffic``: HBM bytes per attn_fwd call from a FETCH_SIZE run and a
+* ``traffic``: HBM bytes per call of a kernel (attn_fwd by default, or
+  ``--kernel attn_qk_prep``) from a FETCH_SIZE run and a
   WRITE_SIZE run, each scaled by what the same counter reads for a plain copy
   of known size recorded in the same process (``bench.py --calibrate-copy``).
 
@@ -36,6 +37,12 @@ def short_name(kernel: str) -> str:
         path = "bound" if len(args) > 3 and args[3] == "true" else "online"
         masked = len(args) > 4 and args[4] == "true"
         return f"attn_fwd[{path}{',masked' if masked else ''}]"
+    m = re.search(r"prep_kernel<([^>]*)>", kernel)
+    if m:
+        args = [x.strip() for x in m.group(1).split(",")]
+        return "attn_qk_prep[norms]" if len(args) > 1 and args[1] == "true" else "attn_qk_prep"
+    if "prep_zero" in kernel:
+        return "attn_qk_prep[init]"
     if "norms_kernel" in kernel:
         return "attn_norms"
     if "zero_head_max" in kernel:
@@ -78,8 +85,9 @@ def counters(directory: str):
     return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in dispatches(directory).items()}
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_bytes: float):
-    """HBM bytes per attn_fwd call (bound + online instantiations)."""
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: float, kernel: str = "attn_fwd"):
+    """HBM bytes per call of ``kernel`` (all kernels whose short name starts
+    with it: attn_fwd's bound and online instantiations, say)."""
     fc = counters(fetch_dir)
     wc = counters(write_dir)
     # the calibration copy is by far the largest copy dispatch of the run
@@ -87,8 +95,8 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: float):
     w_copy = max(dispatches(write_dir)["copy"]["WRITE_SIZE"]) * 1024.0
     f_scale = copy_bytes / f_copy
     w_scale = copy_bytes / w_copy
-    fetch = sum(fc[k]["FETCH_SIZE"] for k in fc if k.startswith("attn_fwd")) * 1024.0 * f_scale
-    write = sum(wc[k]["WRITE_SIZE"] for k in wc if k.startswith("attn_fwd")) * 1024.0 * w_scale
+    fetch = sum(fc[k]["FETCH_SIZE"] for k in fc if k.startswith(kernel)) * 1024.0 * f_scale
+    write = sum(wc[k]["WRITE_SIZE"] for k in wc if k.startswith(kernel)) * 1024.0 * w_scale
     return {"fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write,
             "fetch_scale": f_scale, "write_scale": w_scale,
             "copy_fetch_kib": f_copy / 1024.0, "copy_write_kib": w_copy / 1024.0}
@@ -104,6 +112,7 @@ def main():
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--workload", required=True); t.add_argument("--mode", type=int, required=True)
     t.add_argument("--source-hash", required=True); t.add_argument("--command", required=True)
+    t.add_argument("--kernel", default="attn_fwd")
     a = ap.parse_args()
     if a.cmd == "stats":
         for name, calls, avg, tot in stats(a.dir):
@@ -114,7 +123,7 @@ def main():
             for cn, v in sorted(d.items()):
                 print(f"    {cn:32s} {v:.6g}")
     else:
-        d = traffic(a.fetch_dir, a.write_dir, a.copy_bytes)
+        d = traffic(a.fetch_dir, a.write_dir, a.copy_bytes, a.kernel)
         d.update({"workload": a.workload, "mode": a.mode, "source_hash": a.source_hash, "command": a.command})
         print(json.dumps(d, indent=1))
 

@@ -99,6 +99,7 @@ def _check_norms(qo, ko, nm, want=None):
     (64, 1, 3, 3, 6, 8, "bnhd_out"),      # strided output
     (128, 1, 2, 1, 12, 12, "inplace"),
     (64, 2, 1, 1, 4, 4, "bhnd"),          # a single granule per head
+    (64, 1, 40, 1, 6, 8, "bhnd"),         # many heads per wave, 3 granules
 ])
 def test_qk_prep_small(D, B, H, F, rows, cols, layout):
     pat, q, k, gq, gk, cos, sin = _small_case(D, B, H, F, rows, cols)
