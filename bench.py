@@ -39,12 +39,12 @@ def _code_only(text: str) -> bytes:
     return " ".join(text.split()).encode()
 
 
-# The sources each kernel is built from (the public header's declarations are
-# not part of it): counters taken on a kernel stay valid while these are
-# unchanged.
+# The device sources each kernel is built from (host-side declarations in the
+# headers are not part of it): counters taken on a kernel stay valid while
+# these are unchanged.
 KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "bsvf_device.h", "bsvf_internal.h"],
-    "attn_qk_prep": ["attn_qk_prep.hip", "bsvf_device.h", "bsvf_internal.h"],
+    "attn_fwd": ["attn_fwd.hip", "bsvf_device.h"],
+    "attn_qk_prep": ["attn_qk_prep.hip", "attn_norms.hip", "bsvf_device.h"],
 }
 
 

@@ -7,12 +7,12 @@
 // max |k_n| over each 16-key granule, head_max[B][H][2] = (max|q|, max|k|).
 //
 // HBM-bound: reads Q and K once (2*B*H*N*D*2 bytes) and writes 4*B*H*N*(1+1/16)
-// bytes.  Each wave walks a run of 16-row granules of one head; a row of D bf16
-// is read by D/8 consecutive lanes with 16-byte loads, so one wave-wide load
+// bytes.  Each wave takes one 16-row granule of one head; a row of D bf16 is
+// read by D/8 consecutive lanes with 16-byte loads, so one wave-wide load
 // covers 64/(D/8) whole rows (coalesced, 1 KiB per instruction).  head_max is
-// reduced per workgroup and merged with an unsigned atomicMax on the float bits
-// (valid because norms are >= 0), after a tiny kernel zeroes it on the same
-// stream (no memset, so the pair can be captured in a graph).
+// then reduced from q_norm and k_gmax by a second, small pass (8 workgroups a
+// head): merging the maxima of thousands of workgroups by atomics on the same
+// two words serialises, and costs more than this pass over 1/D of the data.
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
@@ -20,7 +20,7 @@ namespace bsvf {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kGranulesPerWave = 4;
+constexpr int kGranulesPerWave = 1;
 
 struct NormArgs {
   const u16* q;
@@ -32,9 +32,54 @@ struct NormArgs {
   float* head_max;
 };
 
-__global__ void zero_head_max(float* hm, int32_t count) {
-  for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
-    hm[i] = 0.0f;
+// head_max[bh] = (max_n q_norm[bh][n], max_g k_gmax[bh][g]).  Each head's rows
+// are split over kHeadMaxSlices workgroups (a head's q_norm is a few hundred
+// KB, and B*H workgroups alone leave most of the GPU idle); each merges its
+// slice's maxima with an unsigned atomic max on the float bits (norms are >= 0,
+// so the orders agree), into a head_max the producing kernel cleared.  Maxima
+// are exact, so the result does not depend on order.  With VEC the q_norm rows
+// (16-byte aligned) are read 16 bytes per lane.
+constexpr int kHeadMaxThreads = 512;
+constexpr int kHeadMaxSlices = 8;
+
+typedef float f32x4n __attribute__((ext_vector_type(4)));
+
+template <bool VEC>
+__global__ __launch_bounds__(kHeadMaxThreads) void head_max_kernel(const float* __restrict__ q_norm,
+                                                                   const float* __restrict__ k_gmax, int32_t N,
+                                                                   float* __restrict__ head_max) {
+  const int64_t bh = blockIdx.y;
+  const float* qn = q_norm + bh * N;
+  const float* kg = k_gmax + bh * (N / 16);
+  const int t = blockIdx.x * kHeadMaxThreads + threadIdx.x, stride = kHeadMaxSlices * kHeadMaxThreads;
+  float mq = 0.0f, mk = 0.0f;
+  if constexpr (VEC) {
+    const f32x4n* q4 = reinterpret_cast<const f32x4n*>(qn);
+#pragma unroll 4
+    for (int i = t; i < N / 4; i += stride) {
+      const f32x4n v = q4[i];
+      mq = fmaxf(mq, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    }
+  } else {
+#pragma unroll 4
+    for (int i = t; i < N; i += stride) mq = fmaxf(mq, qn[i]);
+  }
+#pragma unroll 2
+  for (int i = t; i < N / 16; i += stride) mk = fmaxf(mk, kg[i]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    mq = fmaxf(mq, __shfl_xor(mq, m));
+    mk = fmaxf(mk, __shfl_xor(mk, m));
+  }
+  __shared__ float red[2][kHeadMaxThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { red[0][wave] = mq; red[1][wave] = mk; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kHeadMaxThreads / 64; ++w) { mq = fmaxf(mq, red[0][w]); mk = fmaxf(mk, red[1][w]); }
+    atomicMax(reinterpret_cast<unsigned int*>(head_max + 2 * bh), __float_as_uint(mq));
+    atomicMax(reinterpret_cast<unsigned int*>(head_max + 2 * bh + 1), __float_as_uint(mk));
+  }
 }
 
 template <int D>
@@ -50,11 +95,11 @@ __global__ __launch_bounds__(kNormThreads) void norms_kernel(NormArgs a) {
   const u16* kh = a.k + b * a.ks_b + h * a.ks_h;
   const int c = lane % LPR, rsub = lane / LPR;
 
-  float qmax = 0.0f, kmax = 0.0f;
+  // the head-max pass that follows merges into a cleared head_max
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.head_max[2 * bh + threadIdx.x] = 0.0f;
   const int g0 = (blockIdx.x * (kNormThreads / 64) + wave) * kGranulesPerWave;
-  // All of this wave's loads are issued before any arithmetic, so each wave
-  // keeps kGranulesPerWave x 2 x 16 rows in flight.  Granules past the end
-  // re-read the last one (in bounds) and are not stored.
+  // All of this wave's loads are issued before any arithmetic.  Granules past
+  // the end re-read the last one (in bounds) and are not stored.
   u32x4 qv[kGranulesPerWave][IPG], kv[kGranulesPerWave][IPG];
 #pragma unroll
   for (int gi = 0; gi < kGranulesPerWave; ++gi) {
@@ -89,28 +134,27 @@ __global__ __launch_bounds__(kNormThreads) void norms_kernel(NormArgs a) {
       const float qn = __builtin_sqrtf(sq), kn = __builtin_sqrtf(sk);
       const int row = g * 16 + it * RPI + rsub;
       if (c == 0) a.q_norm[(int64_t)bh * a.N + row] = qn;
-      qmax = fmaxf(qmax, qn);
       kg = fmaxf(kg, kn);
     }
 #pragma unroll
     for (int m = LPR; m < 64; m <<= 1) kg = fmaxf(kg, __shfl_xor(kg, m));
     if (lane == 0) a.k_gmax[(int64_t)bh * G + g] = kg;
-    kmax = fmaxf(kmax, kg);
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, m));
-  __shared__ float red[2][kNormThreads / 64];
-  if (lane == 0) { red[0][wave] = qmax; red[1][wave] = kmax; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float mq = red[0][0], mk = red[1][0];
-    for (int w = 1; w < kNormThreads / 64; ++w) { mq = fmaxf(mq, red[0][w]); mk = fmaxf(mk, red[1][w]); }
-    atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh), __float_as_uint(mq));
-    atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh + 1), __float_as_uint(mk));
   }
 }
 
 }  // namespace
+
+int launch_head_max(const float* q_norm, const float* k_gmax, int32_t bh, int32_t n, float* head_max,
+                    hipStream_t stream) {
+  // N % 16 == 0, so every head's q_norm row is 16-byte aligned when the base is
+  const dim3 grid(kHeadMaxSlices, bh);
+  if (aligned16(q_norm))
+    hipLaunchKernelGGL(head_max_kernel<true>, grid, dim3(kHeadMaxThreads), 0, stream, q_norm, k_gmax, n, head_max);
+  else
+    hipLaunchKernelGGL(head_max_kernel<false>, grid, dim3(kHeadMaxThreads), 0, stream, q_norm, k_gmax, n, head_max);
+  return 0;
+}
+
 }  // namespace bsvf
 
 using namespace bsvf;
@@ -140,8 +184,6 @@ extern "C" int attn_norms(const void* q, const void* k, int32_t batch, int32_t h
   a.k_gmax = k_gmax;
   a.head_max = head_max;
 
-  const int32_t hm_count = 2 * batch * heads;
-  hipLaunchKernelGGL(zero_head_max, dim3((hm_count + 255) / 256), dim3(256), 0, stream, head_max, hm_count);
   const int granules = seq_len / 16;
   const int per_block = (kNormThreads / 64) * kGranulesPerWave;
   dim3 grid((granules + per_block - 1) / per_block, batch * heads);
@@ -149,6 +191,7 @@ extern "C" int attn_norms(const void* q, const void* k, int32_t batch, int32_t h
     hipLaunchKernelGGL(norms_kernel<128>, grid, dim3(kNormThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(norms_kernel<64>, grid, dim3(kNormThreads), 0, stream, a);
+  launch_head_max(q_norm, k_gmax, batch * heads, seq_len, head_max, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return bsvf::ok();

@@ -15,8 +15,9 @@
 //   bf16 out (nearest even), written through the output strides
 //
 // and, from the rounded rows it has just written, the outputs of attn_norms:
-// |q_n|, the max |k_n| of each 16-key granule and the per-head maxima.  That
-// spares the attention step its separate read of Q and K.
+// |q_n|, the max |k_n| of each 16-key granule and (by the same small
+// reduction kernel attn_norms uses) the per-head maxima.  That spares the
+// attention step its separate read of Q and K.
 //
 // HBM-bound.  A row of D bf16 is handled by D/8 consecutive lanes, 16 bytes
 // (8 elements, 4 rotary pairs) each, so the rotation needs no lane exchange
@@ -32,7 +33,6 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 constexpr int kPrepWaves = kPrepThreads / 64;
-constexpr int kPrepMaxHeads = 2048;  // per-head maxima live in LDS
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -52,10 +52,6 @@ struct PrepArgs {
   float* k_gmax;
   float* head_max;
 };
-
-__global__ void prep_zero(float* p, int32_t count) {
-  for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) p[i] = 0.0f;
-}
 
 // One row chunk through the producer: 8 elements x (bf16 bits in w), weights
 // g, rotary cos/sin of the chunk's 4 pairs.  Returns the packed bf16 result
@@ -99,7 +95,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   constexpr int LPR = D / 8;     // lanes per row
   constexpr int RPI = 64 / LPR;  // rows per wave-wide access
   constexpr int IPG = 16 / RPI;  // accesses per 16-row granule
-  extern __shared__ float hmax_lds[];  // [H][kPrepWaves][2] per-wave maxima
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int G = a.N / 16;
@@ -107,103 +102,77 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(PrepArgs a) {
   const int c = lane % LPR, rsub = lane / LPR;
   const float inv_d = 1.0f / D;
 
-  if constexpr (NORMS) {
-    for (int i = threadIdx.x; i < a.H * kPrepWaves * 2; i += kPrepThreads) hmax_lds[i] = 0.0f;
-    __syncthreads();
-  }
-  if (g < G) {
-    float gq[8], gk[8];
-    {
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c + 4);
-      const f32x4 k0 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c);
-      const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c + 4);
+  // the head-max pass that follows merges into a cleared head_max
+  if (NORMS && blockIdx.x == 0)
+    for (int h = threadIdx.x; h < 2 * a.H; h += kPrepThreads) a.head_max[2 * b * a.H + h] = 0.0f;
+  if (g >= G) return;
+  float gq[8], gk[8];
+  {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(a.gq + 8 * c + 4);
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.gk + 8 * c + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { gq[e] = q0[e]; gq[4 + e] = q1[e]; gk[e] = k0[e]; gk[4 + e] = k1[e]; }
-    }
-    f32x4 cv[IPG], sv[IPG];
+    for (int e = 0; e < 4; ++e) { gq[e] = q0[e]; gq[4 + e] = q1[e]; gk[e] = k0[e]; gk[4 + e] = k1[e]; }
+  }
+  f32x4 cv[IPG], sv[IPG];
+#pragma unroll
+  for (int it = 0; it < IPG; ++it) {
+    const int row = g * 16 + it * RPI + rsub;
+    cv[it] = *reinterpret_cast<const f32x4*>(a.cos + (int64_t)row * (D / 2) + 4 * c);
+    sv[it] = *reinterpret_cast<const f32x4*>(a.sin + (int64_t)row * (D / 2) + 4 * c);
+  }
+  auto load = [&](int h, u32x4 (&qv)[IPG], u32x4 (&kv)[IPG]) {
+    const u16* qi = a.qi + b * a.s[0][0] + h * a.s[0][1];
+    const u16* ki = a.ki + b * a.s[1][0] + h * a.s[1][1];
 #pragma unroll
     for (int it = 0; it < IPG; ++it) {
       const int row = g * 16 + it * RPI + rsub;
-      cv[it] = *reinterpret_cast<const f32x4*>(a.cos + (int64_t)row * (D / 2) + 4 * c);
-      sv[it] = *reinterpret_cast<const f32x4*>(a.sin + (int64_t)row * (D / 2) + 4 * c);
+      qv[it] = *reinterpret_cast<const u32x4*>(qi + (int64_t)row * a.s[0][2] + 8 * c);
+      kv[it] = *reinterpret_cast<const u32x4*>(ki + (int64_t)row * a.s[1][2] + 8 * c);
     }
-    auto load = [&](int h, u32x4 (&qv)[IPG], u32x4 (&kv)[IPG]) {
-      const u16* qi = a.qi + b * a.s[0][0] + h * a.s[0][1];
-      const u16* ki = a.ki + b * a.s[1][0] + h * a.s[1][1];
+  };
+  auto work = [&](int h, const u32x4 (&qv)[IPG], const u32x4 (&kv)[IPG]) {
+    u16* qo = a.qo + b * a.s[2][0] + h * a.s[2][1];
+    u16* ko = a.ko + b * a.s[3][0] + h * a.s[3][1];
+    const int64_t bh = (int64_t)b * a.H + h;
+    float kg = 0.0f;
 #pragma unroll
-      for (int it = 0; it < IPG; ++it) {
-        const int row = g * 16 + it * RPI + rsub;
-        qv[it] = *reinterpret_cast<const u32x4*>(qi + (int64_t)row * a.s[0][2] + 8 * c);
-        kv[it] = *reinterpret_cast<const u32x4*>(ki + (int64_t)row * a.s[1][2] + 8 * c);
-      }
-    };
-    auto work = [&](int h, const u32x4 (&qv)[IPG], const u32x4 (&kv)[IPG]) {
-      u16* qo = a.qo + b * a.s[2][0] + h * a.s[2][1];
-      u16* ko = a.ko + b * a.s[3][0] + h * a.s[3][1];
-      const int64_t bh = (int64_t)b * a.H + h;
-      float qm = 0.0f, kg = 0.0f;
-#pragma unroll
-      for (int it = 0; it < IPG; ++it) {
-        const int row = g * 16 + it * RPI + rsub;
-        float sq, sk;
-        const u32x4 qr = prep_chunk<LPR>(qv[it], gq, cv[it], sv[it], a.eps, inv_d, sq);
-        const u32x4 kr = prep_chunk<LPR>(kv[it], gk, cv[it], sv[it], a.eps, inv_d, sk);
-        *reinterpret_cast<u32x4*>(qo + (int64_t)row * a.s[2][2] + 8 * c) = qr;
-        *reinterpret_cast<u32x4*>(ko + (int64_t)row * a.s[3][2] + 8 * c) = kr;
-        if constexpr (NORMS) {
-#pragma unroll
-          for (int m = LPR / 2; m >= 1; m >>= 1) {
-            sq += __shfl_xor(sq, m);
-            sk += __shfl_xor(sk, m);
-          }
-          const float qn = __builtin_sqrtf(sq), kn = __builtin_sqrtf(sk);
-          if (c == 0) a.q_norm[bh * a.N + row] = qn;
-          qm = fmaxf(qm, qn);
-          kg = fmaxf(kg, kn);
-        }
-      }
+    for (int it = 0; it < IPG; ++it) {
+      const int row = g * 16 + it * RPI + rsub;
+      float sq, sk;
+      const u32x4 qr = prep_chunk<LPR>(qv[it], gq, cv[it], sv[it], a.eps, inv_d, sq);
+      const u32x4 kr = prep_chunk<LPR>(kv[it], gk, cv[it], sv[it], a.eps, inv_d, sk);
+      *reinterpret_cast<u32x4*>(qo + (int64_t)row * a.s[2][2] + 8 * c) = qr;
+      *reinterpret_cast<u32x4*>(ko + (int64_t)row * a.s[3][2] + 8 * c) = kr;
       if constexpr (NORMS) {
 #pragma unroll
-        for (int m = LPR; m < 64; m <<= 1) {
-          qm = fmaxf(qm, __shfl_xor(qm, m));
-          kg = fmaxf(kg, __shfl_xor(kg, m));
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+          sq += __shfl_xor(sq, m);
+          sk += __shfl_xor(sk, m);
         }
-        if (lane == 0) {
-          a.k_gmax[bh * G + g] = kg;
-          float* slot = hmax_lds + 2 * (h * kPrepWaves + wave);  // this wave's own slot
-          slot[0] = fmaxf(slot[0], qm);
-          slot[1] = fmaxf(slot[1], kg);
-        }
+        const float qn = __builtin_sqrtf(sq), kn = __builtin_sqrtf(sk);
+        if (c == 0) a.q_norm[bh * a.N + row] = qn;
+        kg = fmaxf(kg, kn);
       }
-    };
+    }
+    if constexpr (NORMS) {
+#pragma unroll
+      for (int m = LPR; m < 64; m <<= 1) kg = fmaxf(kg, __shfl_xor(kg, m));
+      if (lane == 0) a.k_gmax[bh * G + g] = kg;
+    }
+  };
 #pragma unroll 1
-    for (int h = 0; h < a.H; ++h) {
-      u32x4 qv[IPG], kv[IPG];
-      load(h, qv, kv);
-      work(h, qv, kv);
-    }
-  }
-  if constexpr (NORMS) {
-    __syncthreads();
-    // norms are >= 0, so the float order is the unsigned order of the bits
-    for (int h = threadIdx.x; h < a.H; h += kPrepThreads) {
-      float mq = 0.0f, mk = 0.0f;
-      for (int w = 0; w < kPrepWaves; ++w) {
-        mq = fmaxf(mq, hmax_lds[2 * (h * kPrepWaves + w)]);
-        mk = fmaxf(mk, hmax_lds[2 * (h * kPrepWaves + w) + 1]);
-      }
-      const int64_t bh = (int64_t)b * a.H + h;
-      atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh), __float_as_uint(mq));
-      atomicMax(reinterpret_cast<unsigned int*>(a.head_max + 2 * bh + 1), __float_as_uint(mk));
-    }
+  for (int h = 0; h < a.H; ++h) {
+    u32x4 qv[IPG], kv[IPG];
+    load(h, qv, kv);
+    work(h, qv, kv);
   }
 }
 
 template <int D, bool NORMS>
 void prep_launch(const PrepArgs& a, dim3 grid, hipStream_t stream) {
-  const size_t lds = NORMS ? sizeof(float) * 2 * kPrepWaves * a.H : 0;
-  hipLaunchKernelGGL((prep_kernel<D, NORMS>), grid, dim3(kPrepThreads), lds, stream, a);
+  hipLaunchKernelGGL((prep_kernel<D, NORMS>), grid, dim3(kPrepThreads), 0, stream, a);
 }
 
 bool same_strides(const int64_t* x, const int64_t* y) { return x[0] == y[0] && x[1] == y[1] && x[2] == y[2]; }
@@ -238,8 +207,7 @@ extern "C" int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, voi
   if (!(eps >= 0.0f) || !(eps <= 3.0e38f)) return fail(ATTN_E_INVAL, "eps must be finite and >= 0");
   const int n_norm = (q_norm != nullptr) + (k_gmax != nullptr) + (head_max != nullptr);
   if (n_norm != 0 && n_norm != 3) return fail(ATTN_E_INVAL, "norm outputs must be all given or all NULL");
-  if ((int64_t)batch > 65535) return fail(ATTN_E_SIZE, "batch exceeds 65535");
-  if (heads > kPrepMaxHeads) return fail(ATTN_E_SIZE, "heads exceeds 2048");
+  if ((int64_t)batch * heads > 65535) return fail(ATTN_E_SIZE, "batch * heads exceeds 65535");
   if ((int64_t)batch * heads * seq_len > (int64_t)1 << 40) return fail(ATTN_E_SIZE, "too many rows");
 
   PrepArgs a;
@@ -263,10 +231,6 @@ extern "C" int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, voi
   a.head_max = head_max;
   const dim3 grid(blocks, batch);
   const bool norms = n_norm == 3;
-  if (norms) {
-    const int32_t hm_count = 2 * batch * heads;
-    hipLaunchKernelGGL(prep_zero, dim3((hm_count + 255) / 256), dim3(256), 0, stream, head_max, hm_count);
-  }
   if (head_dim == 128) {
     if (norms) prep_launch<128, true>(a, grid, stream);
     else prep_launch<128, false>(a, grid, stream);
@@ -274,6 +238,7 @@ extern "C" int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, voi
     if (norms) prep_launch<64, true>(a, grid, stream);
     else prep_launch<64, false>(a, grid, stream);
   }
+  if (norms) launch_head_max(q_norm, k_gmax, batch * heads, seq_len, head_max, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return bsvf::ok();

@@ -2,6 +2,8 @@
 // bsvf library.  Not part of the C ABI.
 #pragma once
 
+#include <hip/hip_runtime.h>
+
 #include <cstdint>
 #include <string>
 
@@ -22,5 +24,13 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // element offsets from the head base.
 int check_tensor(const char* name, const void* p, const int64_t* s,
                  int32_t B, int32_t H, int32_t N, int32_t D);
+
+// Enqueues head_max[bh] = (max_n q_norm[bh][n], max_g k_gmax[bh][g]) for the
+// `bh` (batch, head) pairs of contiguous fp32 norms over `n` rows (n % 16 == 0);
+// bh <= 65535.  It merges into head_max with atomic maxima, so the kernel that
+// wrote the norms must have set head_max to zero.  Defined with attn_norms;
+// the producer uses it too.
+int launch_head_max(const float* q_norm, const float* k_gmax, int32_t bh, int32_t n, float* head_max,
+                    hipStream_t stream);
 
 }  // namespace bsvf

@@ -41,8 +41,8 @@ def short_name(kernel: str) -> str:
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         return "attn_qk_prep[norms]" if len(args) > 1 and args[1] == "true" else "attn_qk_prep"
-    if "prep_zero" in kernel:
-        return "attn_qk_prep[init]"
+    if "head_max_kernel" in kernel:
+        return "attn_norms[head_max]"
     if "norms_kernel" in kernel:
         return "attn_norms"
     if "zero_head_max" in kernel:

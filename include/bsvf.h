@@ -302,8 +302,8 @@ int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float*
  * Errors: ATTN_E_INVAL (NULL, non-positive sizes, bad eps, forbidden
  * aliasing, only some norm outputs), ATTN_E_ALIGN (N % 16, misaligned
  * pointer or stride), ATTN_E_UNSUPPORTED (D not 64 or 128), ATTN_E_SIZE
- * (B > 65535, H > 2048 or too many rows), ATTN_E_HIP (launch failed).  All
- * checks run before any launch; on error nothing is written.
+ * (B * H > 65535 or too many rows), ATTN_E_HIP (launch failed).
+ * All checks run before any launch; on error nothing is written.
  */
 int attn_qk_prep(const void* q_in, const void* k_in, void* q_out, void* k_out,
                  int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,

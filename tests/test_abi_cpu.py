@@ -277,7 +277,7 @@ _S = [192 * 64 * 2, 192 * 64, 64]
     (dict(qo=FAKE + 0x100000), 1),                                       # q_out == k_in
     (dict(qo=FAKE, strides=_S * 2 + [192 * 64 * 2, 192 * 64, 128] + _S), 1),  # in place, other strides
     (dict(B=70000, strides=_S * 4), 4),
-    (dict(H=2049, N=16, strides=[2049 * 16 * 64, 16 * 64, 64] * 4), 4),   # per-head maxima beyond LDS
+    (dict(H=70000, N=16, strides=[70000 * 16 * 64, 16 * 64, 64] * 4), 4),   # B * H above 65535
 ])
 def test_qk_prep_validation(over, status):
     assert prep_call(**over) == status
