@@ -811,6 +811,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
 #pragma unroll
     for (int i = 1; i < NW; ++i) { km = fmaxf(km, red[i]); qm = fmaxf(qm, red[NW + i]); }
     if (per_tile) bound = 2.0f * a.scale * qm * km <= ATTN_ELIGIBLE_NATS;
+    // `red` lies in a stage buffer that the first copies below overwrite:
+    // every wave has to have read it first
+    __syncthreads();
   }
   if (bound != BOUND) return;
   if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = bound ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
