@@ -71,6 +71,7 @@ SMALL = [
     (Pattern(1, 528, 0, 0), 1, 2, 128, 256),           # single frame, 16-row tail tile
     (Pattern(7, 112, 2, 0, (3, 6)), 1, 2, 64, 64),     # lopsided window, two globals
     (Pattern(6, 160, 1, 2, (0, 5)), 2, 2, 128, 128),   # 160 = 2.5 stages of 64 keys
+    (Pattern(3, 96, 2, 2), 1, 2, 128, 64),             # window over every frame: dense attention
 ]
 
 
@@ -309,3 +310,31 @@ def test_tile_eligibility_workloads(name):
     O, L = oracle_rows(name, rows)
     e = errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L)
     assert within(e), e
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_uniform_attention_closed_form(mode):
+    """Q = 0 makes every attended score 0: O is the mean of V over the
+    attended keys and LSE = ln(attended keys), the closed forms stored in
+    tests/golden/uniform_lse.json for the tiny pattern."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "uniform_lse.json")))
+    wl = WORKLOADS["tiny"]
+    p = wl.pattern
+    q, k, v = random_qkv(1, 2, p.seq_len, wl.head_dim, seed=7)
+    q = np.zeros_like(q)
+    res = run_gpu(q, k, v, p, wl.scale, mode)
+    T = p.tokens_per_frame
+    vf = np.asarray(v, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    vf = vf.view(np.float32).astype(np.float64)
+    for f in range(p.num_frames):
+        rows = slice(f * T, (f + 1) * T)
+        lse_want = gold["lse_per_frame"][f]
+        assert np.abs(res["lse"][:, :, rows] - lse_want).max() <= 1e-3 * lse_want
+        keys = [g for g in range(p.num_frames) if -p.win_before <= g - f <= p.win_after]
+        assert len(keys) * T == gold["attended_keys_per_frame"][f]
+        mean = np.concatenate([vf[:, :, g * T:(g + 1) * T] for g in keys], axis=2).mean(axis=2)
+        err = np.abs(res["o"][:, :, rows] - mean[:, :, None, :])
+        assert err.max() <= 1e-2 and err.mean() <= 1e-3
+

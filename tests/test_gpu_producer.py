@@ -205,3 +205,23 @@ def test_qk_norm_makes_stress_heads_eligible():
     assert within(e), e
     assert (slack <= ON.ELIGIBLE_NATS * (1 - 1e-3)).all()
     assert (hp == bs.PATH_BOUND).all()
+
+
+def test_qk_prep_zero_rows():
+    """An all-zero row stays zero (eps > 0) and has norm 0; its granule max
+    and the head maxima come from the other rows."""
+    import torch
+    pat, q, k, gq, gk, cos, sin = _small_case(128, 1, 2, 1, 4, 8)
+    q = q.copy(); k = k.copy()
+    q[:, :, 3] = 0
+    k[:, :, 16:32] = 0          # one whole zero granule
+    wq, wk, wqn, wkg, whm = OP.qk_prep(q, k, gq, gk, EPS, cos, sin)
+    qo, ko, nm = _run(q, k, gq, gk, cos, sin)
+    # zero up to sign (0*cos - 0*sin is -0 where cos < 0)
+    assert not (_bits(qo)[:, :, 3] & 0x7FFF).any() and not (_bits(ko)[:, :, 16:32] & 0x7FFF).any()
+    qn, kg, hm = (x.cpu().numpy() for x in nm)
+    assert (qn[:, :, 3] == 0).all() and (kg[:, :, 1] == 0).all()
+    _ulp_check(_bits(qo), wq)
+    _ulp_check(_bits(ko), wk)
+    _check_norms(qo, ko, nm, (wqn, wkg))
+
