@@ -1004,7 +1004,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
-    return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the query tile of this build's kernels");
+    return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the kernels' query tile of 256 rows");
   if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
     if (masked)
       st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
