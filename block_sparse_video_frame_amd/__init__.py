@@ -258,11 +258,45 @@ def _check_qkv(*ts):
             raise ValueError("q, k, v must be bfloat16 CUDA (HIP) tensors")
 
 
+def _same_shape(shape, **ts):
+    """The library sees pointers and strides only: a tensor smaller than the
+    stated sizes would be read or written past its end, so shapes are checked
+    here, before anything else."""
+    for name, t in ts.items():
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _check_aux(device, specs):
+    """Auxiliary tensors: (name, tensor or None, shape, dtype), each contiguous
+    on ``device``."""
+    for name, t, shape, dtype in specs:
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)} on {device}")
+
+
+def _norm_specs(B, H, N, nm, prefix=""):
+    import torch
+    if nm is None:
+        return []
+    if len(nm) != 3:
+        raise ValueError("norms must be the (q_norm, k_gmax, head_max) triple")
+    return [(prefix + "q_norm", nm[0], (B, H, N), torch.float32),
+            (prefix + "k_gmax", nm[1], (B, H, N // 16), torch.float32),
+            (prefix + "head_max", nm[2], (B, H, 2), torch.float32)]
+
+
 def _norms(q, k, out=None):
     """``(q_norm [B,H,N], k_gmax [B,H,N/16], head_max [B,H,2])`` fp32 (``attn_norms``)."""
     import torch
-    _check_qkv(q, k)
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor with unit stride in D")
     B, H, N, D = q.shape
+    _same_shape(q.shape, k=k)
+    _check_qkv(q, k)
+    _check_aux(q.device, _norm_specs(B, H, N, out, "out."))
     if out is None:
         out = (torch.empty(B, H, N, dtype=torch.float32, device=q.device),
                torch.empty(B, H, N // 16, dtype=torch.float32, device=q.device),
@@ -287,10 +321,13 @@ def qk_prep(q_in, k_in, q_gamma, k_gamma, rope_cos, rope_sin, eps: float = 1e-6,
     Outputs default to new contiguous ``[B, H, N, D]`` tensors; passing
     ``q_out=q_in`` (same strides) works in place."""
     import torch
-    _check_qkv(q_in, k_in)
+    if q_in.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor with unit stride in D")
     B, H, N, D = q_in.shape
-    if tuple(k_in.shape) != (B, H, N, D):
-        raise ValueError("q_in and k_in must have the same shape")
+    _same_shape(q_in.shape, k_in=k_in, q_out=q_out, k_out=k_out)
+    _check_qkv(q_in, k_in)
+    if norms:
+        _check_aux(q_in.device, _norm_specs(B, H, N, norms_out, "norms_out."))
     for name, t, shape in (("q_gamma", q_gamma, (D,)), ("k_gamma", k_gamma, (D,)),
                            ("rope_cos", rope_cos, (N, D // 2)), ("rope_sin", rope_sin, (N, D // 2))):
         if t.dtype != torch.float32 or t.device != q_in.device or tuple(t.shape) != shape or not t.is_contiguous():
@@ -323,8 +360,21 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
     (computed here when the mode needs it and none is given).
     """
     import torch
-    _check_qkv(q, k, v)
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, D] tensor with unit stride in D")
     B, H, N, D = q.shape
+    _same_shape(q.shape, k=k, v=v, out=out)
+    if blocks.host.seq_len != N:
+        raise ValueError(f"the block list is for {blocks.host.seq_len} tokens, the tensors have {N}")
+    if blocks.work_order is not None and (blocks.batch, blocks.heads) != (B, H):
+        raise ValueError(f"the block list's launch order is for batch {blocks.batch} x {blocks.heads} heads, "
+                         f"the tensors have {B} x {H}")
+    _check_qkv(q, k, v)
+    if blocks.q_tiles.device != q.device:
+        raise ValueError("the block list lives on another device")
+    _check_aux(q.device, _norm_specs(B, H, N, norms) + [
+        ("lse", lse, (B, H, N), torch.float32), ("shift_out", shift_out, (B, H, N), torch.float32),
+        ("head_path", head_path, (B, H), torch.int32)])
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     nm = norms

@@ -284,6 +284,33 @@ def test_qk_prep_validation(over, status):
     assert bs.lib().attn_last_error().startswith(bs.lib().attn_status_str(status))
 
 
+def test_binding_checks_shapes_before_any_device_work():
+    """The library sees pointers and strides only, so the binding refuses
+    tensors whose shapes disagree (they would be read past their end); these
+    checks come before the device checks, so they run on CPU tensors."""
+    import torch
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    short = torch.zeros(1, 2, 48, 64, dtype=torch.bfloat16)
+    dev = bs.build_blocks_for(Pattern(2, 32, 1, 1), 32).to_device(torch.device("cpu"), 1, 2)
+    with pytest.raises(ValueError, match="shape"):
+        bs.norms(q, short)
+    with pytest.raises(ValueError, match="shape"):
+        bs.attention(q, short, q, dev)
+    with pytest.raises(ValueError, match="shape"):
+        bs.attention(q, q, q, dev, out=short)
+    with pytest.raises(ValueError, match="tokens"):
+        bs.attention(short, short, short, dev)
+    other = bs.build_blocks_for(Pattern(2, 32, 1, 1), 32).to_device(torch.device("cpu"), 1, 4)
+    with pytest.raises(ValueError, match="launch order"):
+        bs.attention(q, q, q, other)
+    g = torch.ones(64)
+    t = torch.ones(64, 32)
+    with pytest.raises(ValueError, match="shape"):
+        bs.qk_prep(q, q, g, g, t, t, q_out=short)
+    with pytest.raises(ValueError, match="CUDA"):
+        bs.attention(q, q, q, dev)
+
+
 # ---- frame-unaware layout (alignment ablation) -------------------------------------------
 
 

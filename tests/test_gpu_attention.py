@@ -189,9 +189,11 @@ def test_errors_with_device_tensors():
     p = Pattern(2, 32, 1, 1)
     q, k, v = (torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda") for _ in range(3))
     blk = bs.build_blocks_for(p, 32).to_device(torch.device("cuda"), 1, 1)
-    with pytest.raises(bs.AttnError) as e:
-        bs.attention(q[:, :, :60], k[:, :, :60], v[:, :, :60], blk, 0.125, 0)
-    assert e.value.status == 2
+    # the binding refuses tensors that do not match the block list or each other
+    with pytest.raises(ValueError, match="tokens"):
+        bs.attention(q[:, :, :48], k[:, :, :48], v[:, :, :48], blk, 0.125, 0)
+    with pytest.raises(ValueError, match="shape"):
+        bs.attention(q, k[:, :, :48], v, blk, 0.125, 0)
     bad = torch.zeros(1, 1, 64, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(bs.AttnError) as e:
         bs.attention(bad, bad, bad, blk, 0.125, 0)
