@@ -1,0 +1,40 @@
+"""bench.py on the CPU: the one-GPU contract and the committed counter files.
+
+The timed run itself needs the GPU; these checks do not."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_kernel_hashes_cover_existing_sources():
+    for kernel in bench.KERNEL_SOURCES:
+        h = bench.source_hash(kernel)
+        assert len(h) == 16 and int(h, 16) >= 0
+
+
+def test_comment_edits_do_not_change_the_hash():
+    src = "int f(int x) { return x + 1; } // one\n/* two */\n"
+    assert bench._code_only(src) == bench._code_only("int f(int x) {\n  return x + 1;\n}\n")
+
+
+def test_committed_traffic_files_are_well_formed():
+    for name in ("attn_fwd_720p_traffic.json", "attn_qk_prep_720p_traffic.json"):
+        d = json.load(open(os.path.join(ROOT, "profiles", name)))
+        assert d["bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"]
+        assert d["bytes_per_launch"] >= d["algorithmic_bytes"] * 0.99
+        assert 1.9 < d["fetch_scale"] < 2.1 and d["write_scale"] == 1.0
+        assert "rocprofv3 --pmc FETCH_SIZE" in d["command_fetch"]
+        assert "rocprofv3 --pmc WRITE_SIZE" in d["command_write"]
