@@ -578,15 +578,27 @@ constexpr int kBuffers = kPrefetch + 2;
 
 // Cuts the tile's valid intervals into consecutive 64-key stages (scalar,
 // uniform state).  Intervals outside [0, N) or not 16-aligned are skipped.
+// Start and length of interval e.  e is the same in every lane; saying so
+// lets the compiler read the list with scalar loads (a vector load's wait
+// would also wait for every stage copy in flight).
+__device__ __forceinline__ void interval_at(const int32_t* __restrict__ kv_iv, int e, int& ks, int& kl) {
+  const int u = __builtin_amdgcn_readfirstlane(e);
+  ks = kv_iv[2 * u];
+  kl = kv_iv[2 * u + 1];
+}
+
 struct KeyWalker {
   const int32_t* __restrict__ kv_iv;
   int e, e1, N, cs, cl, off;
   bool more;
 
   __device__ __forceinline__ void seek() {
-    while (e < e1 && !interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], N)) ++e;
+    for (; e < e1; ++e) {
+      interval_at(kv_iv, e, cs, cl);
+      if (interval_ok(cs, cl, N)) break;
+    }
     more = e < e1;
-    if (more) { cs = kv_iv[2 * e]; cl = kv_iv[2 * e + 1]; off = 0; }
+    off = 0;
   }
   // Next stage.  Returns true when it is one contiguous run of 64 keys (the
   // common case), given by `start`; otherwise fills `d`.
@@ -625,8 +637,11 @@ struct StageCursor {
   bool flag;
 
   __device__ __forceinline__ void seek() {
-    while (e < e1 && !interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], N)) ++e;
-    if (e < e1) { cs = kv_iv[2 * e]; cl = kv_iv[2 * e + 1]; off = 0; flag = kv_flag[e] != 0; }
+    for (; e < e1; ++e) {
+      interval_at(kv_iv, e, cs, cl);
+      if (interval_ok(cs, cl, N)) break;
+    }
+    if (e < e1) { off = 0; flag = kv_flag[__builtin_amdgcn_readfirstlane(e)] != 0; }
   }
   __device__ __forceinline__ void next(int& k0, bool& masked) {
     k0 = cs + off;
