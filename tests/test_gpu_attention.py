@@ -76,7 +76,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 def test_small_all_rows(case, mode):
     p, B, H, D, bq = SMALL[case]
     q, k, v = random_qkv(B, H, p.seq_len, D, seed=100 + case)
@@ -206,7 +206,7 @@ GRANULAR = [c for c in range(len(SMALL)) if SMALL[c][0].tokens_per_frame >= 64]
 
 
 @pytest.mark.parametrize("case", GRANULAR)
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3])
 @pytest.mark.parametrize("granule,bq", [(128, 256), (64, 128)])
 def test_granular_small_all_rows(case, mode, granule, bq):
     p, B, H, D, _ = SMALL[case]
