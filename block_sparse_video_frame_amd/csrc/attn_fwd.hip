@@ -31,6 +31,10 @@
 //   * The upper four waves run half a stage behind the lower four (PV of the
 //     previous stage before QK of this one) so the two halves' MFMA and
 //     exp/VALU phases interleave on each SIMD.
+//   * A tile of at most 64 rows (the short last tile of a frame) runs thin:
+//     the two waves of a pair, on different SIMDs, hold the same 32 rows and
+//     take one 32-key half of every stage each; the pair merges its partial
+//     sums through LDS at the end.  Such a tile otherwise has one busy wave.
 //   * exp is v_exp_f32 on base-2 scores; the tail stage zeroes the scores of
 //     missing 16-key groups (a per-group select, never a per-element mask).
 #include "bsvf_device.h"
@@ -563,6 +567,136 @@ struct Tile {
             oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[qb][kb][kst], oacc[qb][db], 0, 0, 0);
         }
   }
+
+  // ---- Thin tiles (at most 64 rows, one row group per wave pair): each of
+  // the two waves of a pair takes one 32-key block `kb` of every stage, so a
+  // short tile keeps two SIMDs busy instead of one.  Register j of a half
+  // holds key 32kb + 8(j/4) + 4hh + j%4, as in the full-stage layout.
+  using Half = f32x16;
+  using HalfProbs = bf16x8[2];
+
+  __device__ __forceinline__ void scores_half(const lds_char* sm, uint32_t boff, int kb, Half& s) const {
+    static_assert(NQB == 1, "thin tiles take one row group per wave");
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = acc0(0);
+#pragma unroll
+    for (int st = 0; st < C::KSTEPS; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand(sm, boff, kb, st), qreg[0][st], s, 0, 0, 0);
+  }
+
+  // Online path: raise the running max by this half's scores; returns the
+  // factor the accumulator has to be rescaled by.
+  __device__ __forceinline__ float raise_max(const Half& s, float c2) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m2[0], mx * c2);
+    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m2[0] - msafe);
+    m2[0] = mnew;
+    lsum[0] *= alpha;
+    return alpha;
+  }
+
+  // Probabilities of one half stage (see softmax).  TAIL: only the first
+  // `nvalid` keys of the whole stage are real.
+  template <bool BOUND, bool TAIL>
+  __device__ __forceinline__ void softmax_half(const Half& s, HalfProbs& pk, float& alpha, int nvalid, float c2,
+                                               int kb) {
+    alpha = BOUND ? 1.0f : raise_max(s, c2);
+    const float nm = m2[0] == -INFINITY ? 0.0f : -m2[0];
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(BOUND ? s[r] : fmaf(s[r], c2, nm));
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool live = 32 * kb + 8 * i < nvalid;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[4 * i + j] = live ? p[4 * i + j] : 0.0f;
+      }
+    }
+    pk[0] = to_bf16x8(p);
+    pk[1] = to_bf16x8(p + 8);
+    float t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      const u32x4 w = __builtin_bit_cast(u32x4, pk[kst]);
+      t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
+      t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+    }
+    lsum[0] += t0 + t1;
+  }
+
+  // softmax_half of `cur` fused with the scores of block kb of the next
+  // stage, one chunk per MFMA as in softmax_and_scores.
+  template <bool BOUND>
+  __device__ __forceinline__ void softmax_and_scores_half(const Half& cur, const lds_char* sm, uint32_t boff, int kb,
+                                                          Half& nxt, HalfProbs& pk, float& alpha, float c2) {
+    constexpr int NM = C::KSTEPS;
+    constexpr int EPM = 16 / NM;  // softmax elements per MFMA (2 or 4)
+    constexpr int AHEAD = KAHEAD < NM ? KAHEAD : NM;
+    alpha = BOUND ? 1.0f : raise_max(cur, c2);
+    const float nm = m2[0] == -INFINITY ? 0.0f : -m2[0];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nxt[r] = acc0(0);
+    bf16x8 kf[NM];
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) kf[i] = k_operand(sm, boff, kb, i);
+    float part[2] = {0.0f, 0.0f};
+    uint32_t pw[8];
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + AHEAD < NM) kf[i + AHEAD] = k_operand(sm, boff, kb, i + AHEAD);
+      nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[0][i], nxt, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < EPM; e += 2) {
+        const int r = i * EPM + e;
+        const float p0 = __builtin_amdgcn_exp2f(BOUND ? cur[r] : fmaf(cur[r], c2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(BOUND ? cur[r + 1] : fmaf(cur[r + 1], c2, nm));
+        f32x2 f = {p0, p1};
+        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+        pw[r >> 1] = w;
+        part[(e >> 1) & 1] = add_pair(w, part[(e >> 1) & 1]);
+        asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(pw[r >> 1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum[0] += part[0] + part[1];
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      u32x4 w = {pw[4 * kst], pw[4 * kst + 1], pw[4 * kst + 2], pw[4 * kst + 3]};
+      pk[kst] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  __device__ __forceinline__ void rescale_half(float alpha) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) oacc[0][db] *= alpha;
+    }
+  }
+
+  // O^T += V^T * P^T over key block kb of a stage.
+  __device__ __forceinline__ void pv_half(const lds_char* sm, uint32_t boff, int kb, const HalfProbs& pk) {
+    uint32_t va[2][C::DBLK];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) va[h2][db] = boff | (lof.vl[h2] ^ (64u * db));
+    const uint32_t base = C::REGION * 2 + RS * 32 * kb;
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst)
+#pragma unroll
+      for (int db = 0; db < C::DBLK; ++db) {
+        const uint32_t rows = base + RS * 16 * kst;
+        const i16x4 lo4 = ds_read_tr16(sm + va[0][db] + rows);
+        const i16x4 hi4 = ds_read_tr16(sm + va[1][db] + rows);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[kst], oacc[0][db], 0, 0, 0);
+      }
+  }
 };
 
 // s_waitcnt immediate that waits until at most n vector memory accesses of
@@ -759,6 +893,117 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
   T.pv(sm, boff(ns - 1), pk);
 }
 
+// The walk of a thin tile (at most 64 rows).  Wave w works on row group w/2
+// and key block kb = w%2 of every stage; waves past the tile's row groups
+// only copy.  With no lagging half a stage is free once its P*V is done, so
+// copies run three stages ahead.  At the end the kb = 1 wave of each pair
+// hands its partial sum, row sum and shift to its partner through a stage
+// buffer no wave reads any more, and the partner merges them (same shift on
+// the bound path; rescaled to the larger running max on the online path).
+template <int D, int NQB, int NW, bool BOUND>
+__device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
+                                         Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh, int e0, int e1,
+                                         int wave, bool active) {
+  using C = Cfg<D, NQB, NW>;
+  using TT = Tile<D, NQB, NW, BOUND>;
+  constexpr int LOADS = 2 * C::LPW;
+  constexpr int KP = 3;  // stages in flight ahead of the one being consumed
+  static_assert(KP + 1 <= kBuffers, "thin walk needs KP + 1 buffers");
+  const int kb = wave & 1;
+  const uint32_t ksn = (uint32_t)a.sk[2], vsn = (uint32_t)a.sv[2];
+  const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, 2u * (ksn * (uint32_t)(a.N - 1) + D));
+  const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, 2u * (vsn * (uint32_t)(a.N - 1) + D));
+  int total = 0;
+  for (int e = e0; e < e1; ++e)
+    if (interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) total += kv_iv[2 * e + 1];
+  if (total == 0) return;
+  const int ns = (total + BK - 1) / BK, nlast = total - BK * (ns - 1);
+  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::STAGE; };
+  auto boff = [&](int x) { return (uint32_t)((x & (kBuffers - 1)) * C::STAGE * 2); };
+  const lds_char* sm = lds_bytes(smem);
+  KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
+  kw.seek();
+  DmaLanes<D, NQB, NW> dl;
+  dl.init(ksn, vsn, wave, T.lane);
+  auto issue = [&](int x) {
+    StageDesc sd;
+    int start;
+    if (kw.next(sd, start)) issue_stage_run<D, NQB, NW>(kbuf(x), kr, vr, dl, ksn, vsn, start, wave);
+    else issue_stage<D, NQB, NW>(kbuf(x), kr, vr, ksn, vsn, sd, wave, T.lane);
+  };
+#pragma unroll
+  for (int x = 0; x < KP; ++x)
+    if (x < ns) issue(x);
+  // stage 0 landed: at most min(KP, ns) - 1 later stages still in flight
+  if (ns >= 3) __builtin_amdgcn_s_waitcnt(wait_vm(2 * LOADS));
+  else if (ns == 2) __builtin_amdgcn_s_waitcnt(wait_vm(LOADS));
+  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  typename TT::Half sc, sn;
+  typename TT::HalfProbs pk;
+  float alpha;
+  if (active) T.scores_half(sm, boff(0), kb, sc);
+  auto step = [&](int st, typename TT::Half& cur, typename TT::Half& nxt) {
+    // stage st+1 landed (every wave); stage st-1, whose buffer the next copy
+    // fills, is done with (its P*V ran before this barrier)
+    if (st + 2 < ns) __builtin_amdgcn_s_waitcnt(wait_vm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (st + KP < ns) issue(st + KP);
+    if (!active) return;
+    T.template softmax_and_scores_half<BOUND>(cur, sm, boff(st + 1), kb, nxt, pk, alpha, a.c2);
+    if constexpr (!BOUND) T.rescale_half(alpha);
+    T.pv_half(sm, boff(st), kb, pk);
+    pin_pv<2 * C::DBLK>();
+  };
+  int st = 0;
+  for (; st + 2 < ns; st += 2) {
+    step(st, sc, sn);
+    step(st + 1, sn, sc);
+  }
+  if (st + 1 < ns) {
+    step(st, sc, sn);
+    sc = sn;
+  }
+  if (active) {
+    if (nlast == BK) T.template softmax_half<BOUND, false>(sc, pk, alpha, BK, a.c2, kb);
+    else T.template softmax_half<BOUND, true>(sc, pk, alpha, nlast, a.c2, kb);
+    if constexpr (!BOUND) T.rescale_half(alpha);
+    T.pv_half(sm, boff(ns - 1), kb, pk);
+  }
+  // Merge buffer of row group g: stage buffer ns+g (mod 4).  No copy targets
+  // it (the last copy filled stage ns-1) and its last stage, ns+g-4 <= ns-3,
+  // was read before the last barrier of the loop (or never, for short tiles).
+  float* mb = reinterpret_cast<float*>(kbuf(ns + (wave >> 1)));
+  constexpr int NO = C::DBLK * 16;  // accumulator registers per lane
+  if (active && kb == 1) {
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mb[(db * 16 + r) * 64 + T.lane] = T.oacc[0][db][r];
+    mb[NO * 64 + T.lane] = T.lsum[0];
+    mb[(NO + 1) * 64 + T.lane] = T.m2[0];
+  }
+  __syncthreads();
+  if (active && kb == 0) {
+    float f0 = 1.0f, f1 = 1.0f;
+    const float l1 = mb[NO * 64 + T.lane];
+    if constexpr (!BOUND) {
+      const float m1 = mb[(NO + 1) * 64 + T.lane];
+      const float m = fmaxf(T.m2[0], m1);
+      const float msafe = m == -INFINITY ? 0.0f : m;
+      f0 = __builtin_amdgcn_exp2f(T.m2[0] - msafe);
+      f1 = __builtin_amdgcn_exp2f(m1 - msafe);
+      T.m2[0] = m;
+    }
+    T.lsum[0] = T.lsum[0] * f0 + l1 * f1;
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) T.oacc[0][db][r] = T.oacc[0][db][r] * f0 + mb[(db * 16 + r) * 64 + T.lane] * f1;
+  }
+}
+
 // BOUND selects the softmax path this instantiation runs.  Both are launched
 // over the same work; a workgroup whose head takes the other path exits at
 // once, so each head is computed by exactly one of them and each path gets a
@@ -839,7 +1084,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   T.hh = lane >> 5;
   T.lane = lane;
   T.lof = lane_offsets<D>(lane);
-  const int row0 = wave * 32 * NQB;
+  // A tile of at most 64 rows runs thin (see run_thin): waves 2g and 2g+1
+  // both hold row group g.
+  bool thin = false;
+  if constexpr (NQB == 1 && !MASK) thin = nr <= 64;
+  const int row0 = thin ? (wave >> 1) * 32 : wave * 32 * NQB;
   const u16* qh = a.q + b * a.sq[0] + h * a.sq[1];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -881,13 +1130,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // A wave none of whose rows exist (the short last tile of a frame) keeps
   // its share of the loads and barriers but skips the math.
-  const bool active = wv * 32 * NQB < nr;
+  const bool active = thin ? wv < 2 * ((nr + 31) >> 5) : wv * 32 * NQB < nr;
   if constexpr (MASK) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) T.fq[qb] = (qs + min(row0 + qb * 32 + T.n, nr - 1)) / a.frame_T;
   }
-  if (wv >= NW / 2) run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
-  else run_tile<D, NQB, NW, BOUND, false, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+  if (thin) {
+    run_thin<D, NQB, NW, BOUND>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+    if (wv & 1) return;  // merged into the even wave of the pair
+  } else if (wv >= NW / 2) {
+    run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+  } else {
+    run_tile<D, NQB, NW, BOUND, false, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
+  }
 
   // Epilogue: O = O_acc / l (bf16, nearest even), LSE = m + ln l.
   u16* oh = a.o + b * a.so[0] + h * a.so[1];

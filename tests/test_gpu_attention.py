@@ -72,6 +72,8 @@ SMALL = [
     (Pattern(7, 112, 2, 0, (3, 6)), 1, 2, 64, 64),     # lopsided window, two globals
     (Pattern(6, 160, 1, 2, (0, 5)), 2, 2, 128, 128),   # 160 = 2.5 stages of 64 keys
     (Pattern(3, 96, 2, 2), 1, 2, 128, 64),             # window over every frame: dense attention
+    (Pattern(3, 320, 1, 1), 1, 2, 64, 256),            # 64-row tail: two row groups, 10 and 15 stages
+    (Pattern(4, 144, 0, 0), 1, 2, 128, 128),           # 16-row tail over 144 keys: last stage of 16
 ]
 
 
