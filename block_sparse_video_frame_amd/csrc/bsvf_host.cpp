@@ -289,12 +289,6 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
           st.items.push_back((int32_t)(bh * n_qt + u));
           st.cost += cost[u];
         }
-        // Short tiles first: a short tile streams the set's keys at a lower
-        // rate than a full one, so started first it ends before its set does
-        // instead of trailing it.
-        std::stable_sort(st.items.begin(), st.items.end(), [&](int32_t a, int32_t b) {
-          return q_tiles[2 * (a % n_qt) + 1] < q_tiles[2 * (b % n_qt) + 1];
-        });
         sets.push_back(std::move(st));
         t = u;
       }

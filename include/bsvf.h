@@ -160,8 +160,7 @@ int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t
  *   group == 0: the tiles of one (batch, head) that share their key
  *     intervals (one query frame's tiles) form a set that stays together on
  *     one die, so they stream the same K and V through that die's L2; sets,
- *     heaviest first, go to the die with the least cost so far; within a set
- *     the tiles with fewer rows come first (stable).
+ *     heaviest first, go to the die with the least cost so far.
  * Queues are padded with -1 to a common depth (a multiple of `group` when
  * group > 0); such a workgroup exits at once.  The result is a permutation of
  * all items plus padding; it changes only the execution order, never results.
