@@ -342,3 +342,37 @@ def test_uniform_attention_closed_form(mode):
         err = np.abs(res["o"][:, :, rows] - mean[:, :, None, :])
         assert err.max() <= 1e-2 and err.mean() <= 1e-3
 
+
+
+# ---- seeded random patterns ---------------------------------------------------------------
+
+
+def _random_case(i):
+    """Pattern, shape and tile size of random case i (seeded): frame counts,
+    frame sizes, windows, global frames and tile sizes the fixed cases do not
+    pin down, including short tiles of 16-64 rows over long key runs."""
+    rng = np.random.default_rng(5000 + i)
+    F = int(rng.integers(1, 7))
+    T = 16 * int(rng.integers(1, 26))
+    before, after = (int(x) for x in rng.integers(0, 4, size=2))
+    g = tuple(sorted(set(int(x) for x in rng.integers(0, F, size=int(rng.integers(0, 3))))))
+    D = int(rng.choice([64, 128]))
+    bq = 16 * int(rng.integers(1, 17))
+    H = int(rng.integers(1, 4))
+    return Pattern(F, T, before, after, g), 1, H, D, bq
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_patterns_all_rows(case):
+    p, B, H, D, bq = _random_case(case)
+    q, k, v = random_qkv(B, H, p.seq_len, D, seed=6000 + case)
+    scale = 1.0 / math.sqrt(D)
+    O, L = OA.attention(q, k, v, p, scale)
+    for mode in (0, 1, 3):
+        res = run_gpu(q, k, v, p, scale, mode, block_q=bq)
+        e = errors(res["o"], res["lse"], O, L)
+        assert within(e), (p, D, bq, mode, e)
+        if p.tokens_per_frame >= 64:
+            res = run_gpu(q, k, v, p, scale, mode, block_q=bq, granule=64 * (1 + case % 2))
+            e = errors(res["o"], res["lse"], O, L)
+            assert within(e), (p, D, bq, mode, "granular", e)
