@@ -32,9 +32,9 @@
 //     previous stage before QK of this one) so the two halves' MFMA and
 //     exp/VALU phases interleave on each SIMD.
 //   * A tile of at most 64 rows (the short last tile of a frame) runs thin:
-//     the two waves of a pair, on different SIMDs, hold the same 32 rows and
-//     take one 32-key half of every stage each; the pair merges its partial
-//     sums through LDS at the end.  Such a tile otherwise has one busy wave.
+//     four waves, one per SIMD, hold the same 32 rows; each takes one 32-key
+//     half of every other stage, and the four merge their partial sums
+//     through LDS at the end.  Such a tile otherwise has one busy wave.
 //   * exp is v_exp_f32 on base-2 scores; the tail stage zeroes the scores of
 //     missing 16-key groups (a per-group select, never a per-element mask).
 #include "bsvf_device.h"
@@ -568,10 +568,9 @@ struct Tile {
         }
   }
 
-  // ---- Thin tiles (at most 64 rows, one row group per wave pair): each of
-  // the two waves of a pair takes one 32-key block `kb` of every stage, so a
-  // short tile keeps two SIMDs busy instead of one.  Register j of a half
-  // holds key 32kb + 8(j/4) + 4hh + j%4, as in the full-stage layout.
+  // ---- Thin tiles (at most 64 rows; see run_thin): a wave takes one 32-key
+  // block `kb` of a stage.  Register j of a half holds key
+  // 32kb + 8(j/4) + 4hh + j%4, as in the full-stage layout.
   using Half = f32x16;
   using HalfProbs = bf16x8[2];
 
@@ -627,48 +626,6 @@ struct Tile {
       t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
     }
     lsum[0] += t0 + t1;
-  }
-
-  // softmax_half of `cur` fused with the scores of block kb of the next
-  // stage, one chunk per MFMA as in softmax_and_scores.
-  template <bool BOUND>
-  __device__ __forceinline__ void softmax_and_scores_half(const Half& cur, const lds_char* sm, uint32_t boff, int kb,
-                                                          Half& nxt, HalfProbs& pk, float& alpha, float c2) {
-    constexpr int NM = C::KSTEPS;
-    constexpr int EPM = 16 / NM;  // softmax elements per MFMA (2 or 4)
-    constexpr int AHEAD = KAHEAD < NM ? KAHEAD : NM;
-    alpha = BOUND ? 1.0f : raise_max(cur, c2);
-    const float nm = m2[0] == -INFINITY ? 0.0f : -m2[0];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nxt[r] = acc0(0);
-    bf16x8 kf[NM];
-#pragma unroll
-    for (int i = 0; i < AHEAD; ++i) kf[i] = k_operand(sm, boff, kb, i);
-    float part[2] = {0.0f, 0.0f};
-    uint32_t pw[8];
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i + AHEAD < NM) kf[i + AHEAD] = k_operand(sm, boff, kb, i + AHEAD);
-      nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[0][i], nxt, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < EPM; e += 2) {
-        const int r = i * EPM + e;
-        const float p0 = __builtin_amdgcn_exp2f(BOUND ? cur[r] : fmaf(cur[r], c2, nm));
-        const float p1 = __builtin_amdgcn_exp2f(BOUND ? cur[r + 1] : fmaf(cur[r + 1], c2, nm));
-        f32x2 f = {p0, p1};
-        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-        pw[r >> 1] = w;
-        part[(e >> 1) & 1] = add_pair(w, part[(e >> 1) & 1]);
-        asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(pw[r >> 1]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lsum[0] += part[0] + part[1];
-#pragma unroll
-    for (int kst = 0; kst < 2; ++kst) {
-      u32x4 w = {pw[4 * kst], pw[4 * kst + 1], pw[4 * kst + 2], pw[4 * kst + 3]};
-      pk[kst] = __builtin_bit_cast(bf16x8, w);
-    }
   }
 
   __device__ __forceinline__ void rescale_half(float alpha) {
@@ -893,13 +850,16 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
   T.pv(sm, boff(ns - 1), pk);
 }
 
-// The walk of a thin tile (at most 64 rows).  Wave w works on row group w/2
-// and key block kb = w%2 of every stage; waves past the tile's row groups
-// only copy.  With no lagging half a stage is free once its P*V is done, so
-// copies run three stages ahead.  At the end the kb = 1 wave of each pair
-// hands its partial sum, row sum and shift to its partner through a stage
-// buffer no wave reads any more, and the partner merges them (same shift on
-// the bound path; rescaled to the larger running max on the online path).
+// The walk of a thin tile (at most 64 rows).  It consumes two stages per
+// step: wave w works on row group w/4, stage 2j + (w/2)%2 of step j, and key
+// block kb = w%2 of that stage, so a 16-row tile keeps all four SIMDs busy.
+// Waves past the tile's row groups only copy.  A step waits for its two
+// stages, then refills the two buffers the previous step consumed.  At the
+// end the four waves of a row group hold partial sums over disjoint keys: the
+// three with (stage parity, kb) != (0, 0) hand theirs (accumulator, row sum,
+// shift) to the fourth through the stage buffers, and it merges them in a
+// fixed order (same shift on the bound path; rescaled to the largest running
+// max on the online path).
 template <int D, int NQB, int NW, bool BOUND>
 __device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
                                          Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh, int e0, int e1,
@@ -907,9 +867,8 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __rest
   using C = Cfg<D, NQB, NW>;
   using TT = Tile<D, NQB, NW, BOUND>;
   constexpr int LOADS = 2 * C::LPW;
-  constexpr int KP = 3;  // stages in flight ahead of the one being consumed
-  static_assert(KP + 1 <= kBuffers, "thin walk needs KP + 1 buffers");
-  const int kb = wave & 1;
+  static_assert(kBuffers == 4 && NW == 8, "thin walk: two stages consumed, two in flight; 8 waves");
+  const int kb = wave & 1, sp = (wave >> 1) & 1, part = wave & 3;
   const uint32_t ksn = (uint32_t)a.sk[2], vsn = (uint32_t)a.sv[2];
   const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, 2u * (ksn * (uint32_t)(a.N - 1) + D));
   const __amdgpu_buffer_rsrc_t vr = head_rsrc(vh, 2u * (vsn * (uint32_t)(a.N - 1) + D));
@@ -932,51 +891,44 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __rest
     else issue_stage<D, NQB, NW>(kbuf(x), kr, vr, ksn, vsn, sd, wave, T.lane);
   };
 #pragma unroll
-  for (int x = 0; x < KP; ++x)
+  for (int x = 0; x < kBuffers; ++x)
     if (x < ns) issue(x);
-  // stage 0 landed: at most min(KP, ns) - 1 later stages still in flight
-  if (ns >= 3) __builtin_amdgcn_s_waitcnt(wait_vm(2 * LOADS));
-  else if (ns == 2) __builtin_amdgcn_s_waitcnt(wait_vm(LOADS));
-  else __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  typename TT::Half sc, sn;
+  typename TT::Half sc;
   typename TT::HalfProbs pk;
   float alpha;
-  if (active) T.scores_half(sm, boff(0), kb, sc);
-  auto step = [&](int st, typename TT::Half& cur, typename TT::Half& nxt) {
-    // stage st+1 landed (every wave); stage st-1, whose buffer the next copy
-    // fills, is done with (its P*V ran before this barrier)
-    if (st + 2 < ns) __builtin_amdgcn_s_waitcnt(wait_vm(LOADS));
+  for (int s0 = 0; s0 < ns; s0 += 2) {
+    // Stages s0 and s0+1 landed (every wave).  Issued so far: stages 0-3 and
+    // then two per step, i.e. up to min(max(3, s0+1), ns-1); the first step
+    // leaves stages 2 and 3 in flight, later ones none.
+    if (s0 == 0 && ns >= 4) __builtin_amdgcn_s_waitcnt(wait_vm(2 * LOADS));
+    else if (s0 == 0 && ns == 3) __builtin_amdgcn_s_waitcnt(wait_vm(LOADS));
     else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (st + KP < ns) issue(st + KP);
-    if (!active) return;
-    T.template softmax_and_scores_half<BOUND>(cur, sm, boff(st + 1), kb, nxt, pk, alpha, a.c2);
-    if constexpr (!BOUND) T.rescale_half(alpha);
-    T.pv_half(sm, boff(st), kb, pk);
-    pin_pv<2 * C::DBLK>();
-  };
-  int st = 0;
-  for (; st + 2 < ns; st += 2) {
-    step(st, sc, sn);
-    step(st + 1, sn, sc);
+    // the previous step's two buffers are free again
+    if (s0 > 0) {
+      if (s0 + 2 < ns) issue(s0 + 2);
+      if (s0 + 3 < ns) issue(s0 + 3);
+    }
+    const int st = s0 + sp;
+    if (active && st < ns) {
+      T.scores_half(sm, boff(st), kb, sc);
+      if (st == ns - 1 && nlast != BK) T.template softmax_half<BOUND, true>(sc, pk, alpha, nlast, a.c2, kb);
+      else T.template softmax_half<BOUND, false>(sc, pk, alpha, BK, a.c2, kb);
+      if constexpr (!BOUND) T.rescale_half(alpha);
+      T.pv_half(sm, boff(st), kb, pk);
+      pin_pv<2 * C::DBLK>();
+    }
   }
-  if (st + 1 < ns) {
-    step(st, sc, sn);
-    sc = sn;
-  }
-  if (active) {
-    if (nlast == BK) T.template softmax_half<BOUND, false>(sc, pk, alpha, BK, a.c2, kb);
-    else T.template softmax_half<BOUND, true>(sc, pk, alpha, nlast, a.c2, kb);
-    if constexpr (!BOUND) T.rescale_half(alpha);
-    T.pv_half(sm, boff(ns - 1), kb, pk);
-  }
-  // Merge buffer of row group g: stage buffer ns+g (mod 4).  No copy targets
-  // it (the last copy filled stage ns-1) and its last stage, ns+g-4 <= ns-3,
-  // was read before the last barrier of the loop (or never, for short tiles).
-  float* mb = reinterpret_cast<float*>(kbuf(ns + (wave >> 1)));
-  constexpr int NO = C::DBLK * 16;  // accumulator registers per lane
-  if (active && kb == 1) {
+  // Every copy has landed (the last step waited for all of them) and, past
+  // this barrier, no wave reads a stage buffer: the partials go anywhere in
+  // the stage array.  Partial p of row group g: parts 1-3 of the group.
+  __syncthreads();
+  constexpr int NO = C::DBLK * 16;        // accumulator registers per lane
+  constexpr int PSTRIDE = (NO + 2) * 64;  // floats per partial
+  static_assert(2 * 3 * PSTRIDE * 4 <= kBuffers * C::STAGE * 2, "partials must fit in the stage buffers");
+  float* const mb0 = reinterpret_cast<float*>(smem) + (wave >> 2) * 3 * PSTRIDE;
+  if (active && part != 0) {
+    float* mb = mb0 + (part - 1) * PSTRIDE;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -985,22 +937,34 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __rest
     mb[(NO + 1) * 64 + T.lane] = T.m2[0];
   }
   __syncthreads();
-  if (active && kb == 0) {
-    float f0 = 1.0f, f1 = 1.0f;
-    const float l1 = mb[NO * 64 + T.lane];
+  if (active && part == 0) {
+    float f[4] = {1.0f, 1.0f, 1.0f, 1.0f};
     if constexpr (!BOUND) {
-      const float m1 = mb[(NO + 1) * 64 + T.lane];
-      const float m = fmaxf(T.m2[0], m1);
+      float mp[4] = {T.m2[0], 0.0f, 0.0f, 0.0f};
+      float m = mp[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        mp[q] = mb0[(q - 1) * PSTRIDE + (NO + 1) * 64 + T.lane];
+        m = fmaxf(m, mp[q]);
+      }
       const float msafe = m == -INFINITY ? 0.0f : m;
-      f0 = __builtin_amdgcn_exp2f(T.m2[0] - msafe);
-      f1 = __builtin_amdgcn_exp2f(m1 - msafe);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f[q] = __builtin_amdgcn_exp2f(mp[q] - msafe);
       T.m2[0] = m;
     }
-    T.lsum[0] = T.lsum[0] * f0 + l1 * f1;
+    float l = T.lsum[0] * f[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) l += mb0[(q - 1) * PSTRIDE + NO * 64 + T.lane] * f[q];
+    T.lsum[0] = l;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) T.oacc[0][db][r] = T.oacc[0][db][r] * f0 + mb[(db * 16 + r) * 64 + T.lane] * f1;
+      for (int r = 0; r < 16; ++r) {
+        float o = T.oacc[0][db][r] * f[0];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) o += mb0[(q - 1) * PSTRIDE + (db * 16 + r) * 64 + T.lane] * f[q];
+        T.oacc[0][db][r] = o;
+      }
   }
 }
 
@@ -1084,11 +1048,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   T.hh = lane >> 5;
   T.lane = lane;
   T.lof = lane_offsets<D>(lane);
-  // A tile of at most 64 rows runs thin (see run_thin): waves 2g and 2g+1
-  // both hold row group g.
+  // A tile of at most 64 rows runs thin (see run_thin): waves 4g to 4g+3
+  // all hold row group g.
   bool thin = false;
-  if constexpr (NQB == 1 && !MASK) thin = nr <= 64;
-  const int row0 = thin ? (wave >> 1) * 32 : wave * 32 * NQB;
+  if constexpr (NQB == 1 && NW == 8 && !MASK) thin = nr <= 64;
+  const int row0 = thin ? (wave >> 2) * 32 : wave * 32 * NQB;
   const u16* qh = a.q + b * a.sq[0] + h * a.sq[1];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -1130,14 +1094,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // A wave none of whose rows exist (the short last tile of a frame) keeps
   // its share of the loads and barriers but skips the math.
-  const bool active = thin ? wv < 2 * ((nr + 31) >> 5) : wv * 32 * NQB < nr;
+  const bool active = thin ? wv < 4 * ((nr + 31) >> 5) : wv * 32 * NQB < nr;
   if constexpr (MASK) {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) T.fq[qb] = (qs + min(row0 + qb * 32 + T.n, nr - 1)) / a.frame_T;
   }
   if (thin) {
     run_thin<D, NQB, NW, BOUND>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
-    if (wv & 1) return;  // merged into the even wave of the pair
+    if (wv & 3) return;  // merged into the first wave of the row group
   } else if (wv >= NW / 2) {
     run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
   } else {

@@ -247,16 +247,21 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
   const int64_t items = (int64_t)n_qt * heads * batch;
   if (items > 2147483647LL) return fail(ATTN_E_SIZE, "too many work items");
 
-  // Cost of a tile: attended keys x max(rows, largest tile / 2).  A tile's
-  // run time follows its key count; a short tile saves time only once it
-  // leaves half of its workgroup's waves idle.
+  // Cost of a tile: attended keys x max(rows, R/2), R the largest tile's
+  // rows.  A tile's run time follows its key count; a short tile saves time
+  // only once it leaves half of its workgroup's waves idle.  A tile of at most
+  // R/4 rows (the kernel walks it with all its waves on a quarter of the
+  // rows' work each) costs about a third of a full one: keys x R/3.
   int64_t max_rows = 1;
   for (int32_t t = 0; t < n_qt; ++t) max_rows = std::max<int64_t>(max_rows, q_tiles[2 * t + 1]);
   std::vector<int64_t> cost(n_qt);
+  std::vector<char> is_short(n_qt);
   for (int32_t t = 0; t < n_qt; ++t) {
     int64_t keys = 0;
     for (int32_t e = kv_ptr[t]; e < kv_ptr[t + 1]; ++e) keys += kv_iv[2 * e + 1];
-    cost[t] = keys * std::max<int64_t>(q_tiles[2 * t + 1], max_rows / 2);
+    const int64_t rows = q_tiles[2 * t + 1];
+    is_short[t] = 4 * rows <= max_rows;
+    cost[t] = keys * (is_short[t] ? max_rows / 3 : std::max<int64_t>(rows, max_rows / 2));
   }
 
   // One queue of items per die; workgroup slot*num_xcd + x takes item
@@ -275,32 +280,49 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
     // query frame) read the same K and V: keep each such set together on one
     // die, so its tiles stream those keys through that die's L2 at the same
     // time.  Sets go, heaviest first, to the die with the least work so far.
-    struct Set { int64_t cost; int32_t first; std::vector<int32_t> items; };
+    // Short tiles stay out of the sets: dealt last, heaviest first, each to
+    // the die with the least work, they even out the ends of the queues.
+    struct Set { int64_t cost; std::vector<int32_t> items; };
     std::vector<Set> sets;
+    std::vector<int32_t> fill;
     for (int64_t bh = 0; bh < (int64_t)batch * heads; ++bh) {
       int32_t t = 0;
       while (t < n_qt) {
-        Set st{0, (int32_t)(bh * n_qt + t), {}};
+        Set st{0, {}};
         int32_t u = t;
         for (; u < n_qt; ++u) {
           const int32_t n0 = kv_ptr[t + 1] - kv_ptr[t], n1 = kv_ptr[u + 1] - kv_ptr[u];
           if (n0 != n1 || !std::equal(kv_iv + 2 * kv_ptr[t], kv_iv + 2 * kv_ptr[t + 1], kv_iv + 2 * kv_ptr[u]))
             break;
-          st.items.push_back((int32_t)(bh * n_qt + u));
-          st.cost += cost[u];
+          if (is_short[u]) {
+            fill.push_back((int32_t)(bh * n_qt + u));
+          } else {
+            st.items.push_back((int32_t)(bh * n_qt + u));
+            st.cost += cost[u];
+          }
         }
-        sets.push_back(std::move(st));
+        if (!st.items.empty()) sets.push_back(std::move(st));
         t = u;
       }
     }
     std::stable_sort(sets.begin(), sets.end(), [](const Set& a, const Set& b) { return a.cost > b.cost; });
+    std::stable_sort(fill.begin(), fill.end(), [&](int32_t a, int32_t b) { return cost[a % n_qt] > cost[b % n_qt]; });
     std::vector<int64_t> load(num_xcd, 0);
-    for (const Set& st : sets) {
+    auto least = [&]() {
       int x = 0;
       for (int j = 1; j < num_xcd; ++j)
         if (load[j] < load[x]) x = j;
+      return x;
+    };
+    for (const Set& st : sets) {
+      const int x = least();
       load[x] += st.cost;
       queue[x].insert(queue[x].end(), st.items.begin(), st.items.end());
+    }
+    for (int32_t w : fill) {
+      const int x = least();
+      load[x] += cost[w % n_qt];
+      queue[x].push_back(w);
     }
   }
   size_t depth = 0;

@@ -152,7 +152,8 @@ int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t
  * attn_build_schedule — host, integer only, deterministic.
  * Launch order for attn_fwd over batch*heads*n_qt work items (item
  * w = tile + n_qt * (head + heads * batch_index)).  A tile's cost is
- * keys * max(rows, R/2), R the largest tile's rows.  Workgroup i runs on
+ * keys * max(rows, R/2), R the largest tile's rows, or keys * R/3 for a short
+ * tile (at most R/4 rows).  Workgroup i runs on
  * accelerator die i % num_xcd and takes the next item of that die's queue:
  *   group > 0: items by decreasing cost (ties keep the natural order), cut
  *     into groups of `group` consecutive items, group j appended to die
@@ -160,7 +161,9 @@ int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t
  *   group == 0: the tiles of one (batch, head) that share their key
  *     intervals (one query frame's tiles) form a set that stays together on
  *     one die, so they stream the same K and V through that die's L2; sets,
- *     heaviest first, go to the die with the least cost so far.
+ *     heaviest first, go to the die with the least cost so far.  Short tiles
+ *     are left out of the sets and dealt after them, heaviest first, each to
+ *     the die with the least cost so far.
  * Queues are padded with -1 to a common depth (a multiple of `group` when
  * group > 0); such a workgroup exits at once.  The result is a permutation of
  * all items plus padding; it changes only the execution order, never results.

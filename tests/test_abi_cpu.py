@@ -102,6 +102,18 @@ def test_builder_capacity_protocol():
     assert L.attn_build_blocks(None, 32, None, None, None, None, ctypes.byref(n_qt), ctypes.byref(nnz)) == 1
 
 
+def _tile_costs(blk):
+    """Scheduling cost of each tile: keys * max(rows, R/2), or keys * R/3 for
+    a short tile of at most R/4 rows (R the largest tile's rows)."""
+    R = int(blk.q_tiles[:, 1].max())
+    cost = {}
+    for t in range(blk.n_qt):
+        keys = int(blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum())
+        rows = int(blk.q_tiles[t, 1])
+        cost[t] = keys * (R // 3 if 4 * rows <= R else max(rows, R // 2))
+    return cost
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_schedule_is_a_padded_permutation(name):
     wl = WORKLOADS[name]
@@ -114,11 +126,7 @@ def test_schedule_is_a_padded_permutation(name):
         assert sorted(real.tolist()) == list(range(items))
         assert (order[order < 0] == -1).all()
         # every die's queue runs longest work first
-        cost = {}
-        half = int(blk.q_tiles[:, 1].max()) // 2
-        for t in range(blk.n_qt):
-            keys = blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum()
-            cost[t] = int(keys) * max(int(blk.q_tiles[t, 1]), half)
+        cost = _tile_costs(blk)
         for x in range(xcd):
             seq = [cost[w % blk.n_qt] for w in order[x::xcd] if w >= 0]
             assert all(a >= b for a, b in zip(seq, seq[1:]))
@@ -128,44 +136,49 @@ def test_schedule_is_a_padded_permutation(name):
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_frame_set_schedule(name):
+@pytest.mark.parametrize("block_q", [256, 64])
+def test_frame_set_schedule(name, block_q):
     """group 0: a permutation; each set of tiles with equal key intervals of one
-    head sits contiguously on a single die; die loads balanced within one set."""
+    head (short tiles left out) sits contiguously on a single die; the short
+    tiles come after every set, heaviest first; die loads end within the
+    largest set or short tile of each other."""
     wl = WORKLOADS[name]
-    blk = bs.build_blocks_for(wl.pattern, 256)
+    blk = bs.build_blocks_for(wl.pattern, block_q)
     items = blk.n_qt * wl.heads * wl.batch
     xcd = 8
     order = bs.build_schedule(blk, wl.batch, wl.heads, 0, xcd)
     assert len(order) % xcd == 0
     real = order[order >= 0]
     assert sorted(real.tolist()) == list(range(items))
-    half = int(blk.q_tiles[:, 1].max()) // 2
-    key = {}
-    cost = {}
-    for t in range(blk.n_qt):
-        ivs = tuple(map(tuple, blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1]].tolist()))
-        key[t] = ivs
-        cost[t] = int(blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1], 1].sum()) * max(int(blk.q_tiles[t, 1]), half)
-    loads, biggest = [], 0
+    R = int(blk.q_tiles[:, 1].max())
+    short = {t: 4 * int(blk.q_tiles[t, 1]) <= R for t in range(blk.n_qt)}
+    key = {t: tuple(map(tuple, blk.kv_iv[blk.kv_ptr[t]:blk.kv_ptr[t + 1]].tolist())) for t in range(blk.n_qt)}
+    cost = _tile_costs(blk)
+    loads = []
     seen = set()
     for x in range(xcd):
         q = [w for w in order[x::xcd] if w >= 0]
         assert all(w == -1 for w in order[x::xcd][len(q):])       # padding only at the end
         loads.append(sum(cost[w % blk.n_qt] for w in q))
+        flags = [short[w % blk.n_qt] for w in q]
+        n_long = flags.count(False)
+        assert not any(flags[:n_long])                            # short tiles after the sets
+        tail = [cost[w % blk.n_qt] for w in q[n_long:]]
+        assert all(a >= b for a, b in zip(tail, tail[1:]))        # heaviest first
         runs = []
-        for w in q:
+        for w in q[:n_long]:
             s = (w // blk.n_qt, key[w % blk.n_qt])
             if not runs or runs[-1] != s:
                 runs.append(s)
         assert len(runs) == len(set(runs))                        # each set contiguous
         assert not (set(runs) & seen)                             # and on one die only
         seen |= set(runs)
-    sets = {}
+    units = {}
     for w in range(items):
-        s = (w // blk.n_qt, key[w % blk.n_qt])
-        sets[s] = sets.get(s, 0) + cost[w % blk.n_qt]
-    biggest = max(sets.values())
-    assert max(loads) - min(loads) <= biggest
+        t = w % blk.n_qt
+        u = ("short", w) if short[t] else (w // blk.n_qt, key[t])
+        units[u] = units.get(u, 0) + cost[t]
+    assert max(loads) - min(loads) <= max(units.values())
 
 
 def test_schedule_errors():
