@@ -33,7 +33,7 @@ SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE = 0, 1, 
 PATH_ONLINE, PATH_BOUND = 0, 1
 MAX_BLOCK_Q = 256
 ELIGIBLE_NATS = 60.0
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -63,6 +63,7 @@ class _Blocks(ctypes.Structure):
         ("q_tiles", ctypes.c_void_p), ("kv_ptr", ctypes.c_void_p), ("kv_iv", ctypes.c_void_p),
         ("n_qt", ctypes.c_int32), ("nnz", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("work_order", ctypes.c_void_p), ("n_work", ctypes.c_int32),
+        ("num_xcd", ctypes.c_int32), ("work_ctr", ctypes.c_void_p),
     ]
 
 
@@ -149,7 +150,11 @@ class Blocks:
         return int(self.kv_iv.shape[0])
 
     def to_device(self, device, batch: int, heads: int, schedule: bool = True, group: int = 0,
-                  num_xcd: int = 8) -> "DeviceBlocks":
+                  num_xcd: int = 8, persistent: bool = True) -> "DeviceBlocks":
+        """Device copy of the list.  With ``schedule`` the launch order comes from
+        :func:`build_schedule`; with ``persistent`` as well, attention runs one
+        workgroup per CU taking items from the order's per-die queues (see
+        ``attn_blocks_t.work_ctr``), otherwise one workgroup per item."""
         import torch
         order = build_schedule(self, batch, heads, group, num_xcd) if schedule else None
 
@@ -158,7 +163,8 @@ class Blocks:
 
         return DeviceBlocks(self, up(self.q_tiles), up(self.kv_ptr), up(self.kv_iv),
                             up(order) if order is not None else None, batch, heads,
-                            up(self.kv_flag) if self.kv_flag is not None else None)
+                            up(self.kv_flag) if self.kv_flag is not None else None,
+                            num_xcd, persistent and order is not None)
 
 
 @dataclass
@@ -171,12 +177,15 @@ class DeviceBlocks:
     batch: int
     heads: int
     kv_flag: object = None
+    num_xcd: int = 8
+    persistent: bool = False
 
-    def c_struct(self) -> _Blocks:
+    def c_struct(self, work_ctr=None) -> _Blocks:
         return _Blocks(self.q_tiles.data_ptr(), self.kv_ptr.data_ptr(), self.kv_iv.data_ptr(),
                        self.host.n_qt, self.host.nnz, self.host.block_q,
                        self.work_order.data_ptr() if self.work_order is not None else None,
-                       int(self.work_order.numel()) if self.work_order is not None else 0)
+                       int(self.work_order.numel()) if self.work_order is not None else 0,
+                       self.num_xcd, work_ctr.data_ptr() if work_ctr is not None else None)
 
 
 def build_blocks(num_frames: int, tokens_per_frame: int, win_before: int, win_after: int,
@@ -385,7 +394,10 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
     if lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
-    cb = blocks.c_struct()
+    # slot counters of the persistent launch, one set per call so that calls
+    # on different streams never share them (the library zeroes them)
+    ctr = torch.empty(blocks.num_xcd, dtype=torch.int32, device=q.device) if blocks.persistent else None
+    cb = blocks.c_struct(ctr)
     qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
     so = shift_out.data_ptr() if shift_out is not None else None
     hp = head_path.data_ptr() if head_path is not None else None

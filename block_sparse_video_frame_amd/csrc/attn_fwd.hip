@@ -62,6 +62,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 // scale*log2(e)*|q|*|k| by that much; the margin covers it with room for the
 // fp32 dot-product and norm rounding (below D * 2^-24 for D <= 128).
 constexpr float kBoundMargin = 1.0f + 1.0f / 256.0f;
+// s_getreg operand for the XCC id hardware register (id 20, bits 31:0)
+constexpr int kHwRegXccId = (31 << 11) | 20;
+
+// Read-only inputs (block lists, norms) are read through constant-address-
+// space pointers: the compiler then treats every load from them as invariant
+// and keeps uniform ones on the scalar unit, whichever way the pointer came.
+typedef __attribute__((address_space(4))) const int32_t ci32;
+typedef __attribute__((address_space(4))) const float cf32;
 
 struct FwdArgs {
   const u16* q;
@@ -80,6 +88,8 @@ struct FwdArgs {
   int32_t n_qt, nnz, block_q;
   const int32_t* work_order;
   int32_t n_work;
+  int32_t n_xcd;            // queues in work_order (persistent launch)
+  int32_t* work_ctr;        // their slot counters (persistent launch)
   const float* q_norm;
   const float* k_gmax;
   const float* head_max;
@@ -672,14 +682,14 @@ constexpr int kBuffers = kPrefetch + 2;
 // Start and length of interval e.  e is the same in every lane; saying so
 // lets the compiler read the list with scalar loads (a vector load's wait
 // would also wait for every stage copy in flight).
-__device__ __forceinline__ void interval_at(const int32_t* __restrict__ kv_iv, int e, int& ks, int& kl) {
+__device__ __forceinline__ void interval_at(const ci32* kv_iv, int e, int& ks, int& kl) {
   const int u = __builtin_amdgcn_readfirstlane(e);
   ks = kv_iv[2 * u];
   kl = kv_iv[2 * u + 1];
 }
 
 struct KeyWalker {
-  const int32_t* __restrict__ kv_iv;
+  const ci32* kv_iv;
   int e, e1, N, cs, cl, off;
   bool more;
 
@@ -722,8 +732,8 @@ struct KeyWalker {
 // The start key and mask flag of the stages in the order they are consumed
 // (the frame-unaware layout, whose stages each lie inside one interval).
 struct StageCursor {
-  const int32_t* __restrict__ kv_iv;
-  const int32_t* __restrict__ kv_flag;
+  const ci32* kv_iv;
+  const ci32* kv_flag;
   int e, e1, N, cs, cl, off;
   bool flag;
 
@@ -752,7 +762,7 @@ struct StageCursor {
 // the other's matrix work instead of both contending for the same unit.
 // Every stage but the tile's last is full.
 template <int D, int NQB, int NW, bool BOUND, bool LAG, bool MASK>
-__device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
+__device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u16* smem,
                                          Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh,
                                          int e0, int e1, int wave, bool active) {
   using C = Cfg<D, NQB, NW>;
@@ -773,7 +783,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
   const lds_char* sm = lds_bytes(smem);
   KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
   kw.seek();
-  StageCursor cur_stage{kv_iv, a.kv_flag, e0, e1, a.N, 0, 0, 0, false};
+  StageCursor cur_stage{kv_iv, (const ci32*)a.kv_flag, e0, e1, a.N, 0, 0, 0, false};
   if constexpr (MASK) cur_stage.seek();
   // frame mask of stage x (consumed in order), before its softmax
   auto mask_stage = [&](typename Tile<D, NQB, NW, BOUND>::Scores& sc_x, int x) {
@@ -861,7 +871,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const int32_t* __rest
 // fixed order (same shift on the bound path; rescaled to the largest running
 // max on the online path).
 template <int D, int NQB, int NW, bool BOUND>
-__device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __restrict__ kv_iv, u16* smem,
+__device__ __forceinline__ void run_thin(const FwdArgs& a, const ci32* kv_iv, u16* smem,
                                          Tile<D, NQB, NW, BOUND>& T, const u16* kh, const u16* vh, int e0, int e1,
                                          int wave, bool active) {
   using C = Cfg<D, NQB, NW>;
@@ -968,32 +978,30 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const int32_t* __rest
   }
 }
 
-// BOUND selects the softmax path this instantiation runs.  Both are launched
-// over the same work; a workgroup whose head takes the other path exits at
-// once, so each head is computed by exactly one of them and each path gets a
-// register allocation of its own.
+// One work item w (a query tile of one (batch, head)) on the softmax path
+// BOUND, in the stage array `smem`.  Returns false, having written nothing,
+// when the item takes the other path; true when it is done (or is no valid
+// item).  All waves of the workgroup call it and return together, except
+// that waves with no rows may return before the epilogue.
 template <int D, int NQB, int NW, bool BOUND, bool MASK>
-__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* __restrict__ q_tiles,
-                                                      const int32_t* __restrict__ kv_ptr,
-                                                      const int32_t* __restrict__ kv_iv,
-                                                      const int32_t* __restrict__ work_order,
-                                                      const float* __restrict__ k_gmax,
-                                                      const float* __restrict__ head_max) {
+__device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, const ci32* kv_ptr,
+                                         const ci32* kv_iv, const cf32* k_gmax, const cf32* head_max,
+                                         u16* smem, int w) {
+  const cf32* q_norm = (const cf32*)a.q_norm;
   using C = Cfg<D, NQB, NW>;
-  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The thread index is made opaque, so that the per-lane setup derived from
+  // it is computed per item instead of being hoisted out of a persistent
+  // workgroup's item loop and held in registers across it.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
 
-  int w = blockIdx.x;
-  if (work_order) {
-    if (w >= a.n_work) return;
-    w = work_order[w];
-  }
   const int total = a.n_qt * a.H * a.B;
-  if (w < 0 || w >= total) return;
+  if (w < 0 || w >= total) return true;
   const int tile = w % a.n_qt, bh = w / a.n_qt;
   const int b = bh / a.H, h = bh % a.H;
   const int qs = q_tiles[2 * tile], nr = q_tiles[2 * tile + 1];
-  if (qs < 0 || nr <= 0 || nr > C::BQ || nr > a.block_q || qs > a.N - nr) return;
+  if (qs < 0 || nr <= 0 || nr > C::BQ || nr > a.block_q || qs > a.N - nr) return true;
   int e0 = kv_ptr[tile], e1 = kv_ptr[tile + 1];
   e0 = max(0, min(e0, a.nnz));
   e1 = max(e0, min(e1, a.nnz));
@@ -1008,13 +1016,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
     bound = 2.0f * a.scale * mq * mk <= ATTN_ELIGIBLE_NATS;
   }
-  if (!per_tile && bound != BOUND) return;
+  if (!per_tile && bound != BOUND) return false;
 
   // Tile-wide max key norm over every attended 16-key granule.
   float km = 0.0f;
   if (BOUND || per_tile) {
     float* red = reinterpret_cast<float*>(smem + C::STAGE);
-    const float* kg = k_gmax + (int64_t)bh * (a.N / 16);
+    const cf32* kg = k_gmax + (int64_t)bh * (a.N / 16);
     for (int e = e0; e < e1; ++e) {
       const int ks = kv_iv[2 * e], kl = kv_iv[2 * e + 1];
       if (!interval_ok(ks, kl, a.N)) continue;
@@ -1022,7 +1030,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     }
     float qm = 0.0f;
     if (per_tile)
-      for (int r = tid; r < nr; r += C::NT) qm = fmaxf(qm, a.q_norm[(int64_t)bh * a.N + qs + r]);
+      for (int r = tid; r < nr; r += C::NT) qm = fmaxf(qm, q_norm[(int64_t)bh * a.N + qs + r]);
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
       km = fmaxf(km, __shfl_xor(km, m));
@@ -1039,7 +1047,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     // every wave has to have read it first
     __syncthreads();
   }
-  if (bound != BOUND) return;
+  if (bound != BOUND) return false;
   if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = bound ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
   const float kfac = BOUND ? a.scale * km * kBoundMargin : 0.0f;
 
@@ -1076,7 +1084,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
       T.qreg[qb][st] = valid ? x : z;
     }
     if constexpr (BOUND) {
-      const float qn = a.q_norm[(int64_t)bh * a.N + qs + (valid ? r : 0)];
+      const float qn = q_norm[(int64_t)bh * a.N + qs + (valid ? r : 0)];
       T.m2[qb] = valid ? qn * kfac * kLog2e : 0.0f;
     } else {
       T.m2[qb] = -INFINITY;
@@ -1101,7 +1109,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
   }
   if (thin) {
     run_thin<D, NQB, NW, BOUND>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
-    if (wv & 3) return;  // merged into the first wave of the row group
+    if (wv & 3) return true;  // merged into the first wave of the row group
   } else if (wv >= NW / 2) {
     run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
   } else {
@@ -1134,6 +1142,116 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
       if (a.shift_out) a.shift_out[ri] = T.m2[qb] * kLn2;
     }
   }
+  return true;
+}
+
+// Static launch: workgroup i takes item work_order[i] (or i) on the path
+// BOUND.  Both paths are launched over the same work; a workgroup whose item
+// takes the other path exits at once, so each item is computed by exactly one
+// of them and each path gets a register allocation of its own.
+template <int D, int NQB, int NW, bool BOUND, bool MASK>
+__global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* __restrict__ q_tiles,
+                                                      const int32_t* __restrict__ kv_ptr,
+                                                      const int32_t* __restrict__ kv_iv,
+                                                      const int32_t* __restrict__ work_order,
+                                                      const float* __restrict__ k_gmax,
+                                                      const float* __restrict__ head_max) {
+  using C = Cfg<D, NQB, NW>;
+  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
+  int w = blockIdx.x;
+  if (work_order) {
+    if (w >= a.n_work) return;
+    w = work_order[w];
+  }
+  run_item<D, NQB, NW, BOUND, MASK>(a, (const ci32*)q_tiles, (const ci32*)kv_ptr, (const ci32*)kv_iv,
+                                    (const cf32*)k_gmax, (const cf32*)head_max, smem, w);
+}
+
+// The kernel-argument segment (constant address space: scalar loads that no
+// store of the kernel can alias).
+typedef __attribute__((address_space(4))) const char kernarg_char;
+typedef __attribute__((address_space(4))) const FwdArgs kernarg_args;
+
+// Persistent launch: one workgroup per CU, each taking items until none is
+// left.  work_order holds n_xcd queues (slot j of queue x at j * n_xcd + x,
+// padding -1 only at a queue's end); work_ctr[x] counts the slots of queue x
+// handed out.  A workgroup takes slots from the queue of its own accelerator
+// die (XCC) first -- the schedule keeps the tiles of one frame, which read
+// the same keys, in one queue -- and then from the others, so a die that runs
+// faster takes over work a slower one has not reached instead of idling
+// while it finishes.  It computes the items on the path BOUND and passes
+// over the others (the static launch of the other path takes those); the
+// outputs do not depend on which workgroup computes an item.  (One kernel
+// for both paths would need more registers than the bound path alone.)
+template <int D, int NQB, int NW, bool BOUND, bool MASK>
+__global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
+  using C = Cfg<D, NQB, NW>;
+  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
+  uint32_t empty = 0;  // thread 0: the queues found exhausted
+  // The item goes to every wave through the first word of the stage array
+  // (a separate LDS variable would cost the operand reads their overlap with
+  // the stage copies: see tile_max).
+  int32_t* const word = reinterpret_cast<int32_t*>(smem);
+  for (;;) {
+    __syncthreads();  // every wave is done with the previous item's LDS
+    if (threadIdx.x == 0) {
+      // The queue layout and pointers are read here, through a pointer to
+      // the kernel arguments the compiler cannot see through, rather than
+      // held in scalar registers across the item (the walk needs them all).
+      // (`a`, the only kernel argument, starts the segment)
+      const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
+      asm volatile("" : "+s"(args));
+      const kernarg_args& ka = *reinterpret_cast<const kernarg_args*>(args);
+      const ci32* order = (const ci32*)ka.work_order;
+      int32_t* counters = ka.work_ctr;
+      const int nx = ka.n_xcd, depth = ka.n_work / nx;
+      const int mine = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & 0xF) % nx;
+      int w = -1;
+      for (int k = 0; k < nx && w < 0; ++k) {
+        const int x = (mine + k) % nx;
+        if ((empty >> x) & 1) continue;
+        const int slot = atomicAdd(counters + x, 1);
+        const int cand = slot < depth ? order[slot * nx + x] : -1;
+        if (cand < 0) empty |= 1u << x;
+        else w = cand;
+      }
+      word[0] = w;
+    }
+    __syncthreads();
+    const int w = __builtin_amdgcn_readfirstlane(word[0]);
+    __syncthreads();  // read by every wave before the item's copies reuse it
+    if (w < 0) break;
+    // The item reads its arguments through the same opaque pointer, so none
+    // is held in a scalar register from one item to the next.
+    const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(args));
+    FwdArgs ia;
+    static_assert(sizeof(FwdArgs) % 4 == 0, "FwdArgs is copied in dwords");
+    {
+      typedef __attribute__((address_space(4))) const uint32_t kernarg_u32;
+      const kernarg_u32* src = (const kernarg_u32*)args;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&ia);
+#pragma unroll
+      for (int i = 0; i < (int)(sizeof(FwdArgs) / 4); ++i) dst[i] = src[i];
+    }
+    run_item<D, NQB, NW, BOUND, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr, (const ci32*)ia.kv_iv,
+                                      (const cf32*)ia.k_gmax, (const cf32*)ia.head_max, smem, w);
+  }
+}
+
+__global__ void zero_i32(int32_t* __restrict__ p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+template <int D, int NQB, int NW, bool MASK>
+int launch_persistent(const FwdArgs& a, int grid, hipStream_t stream) {
+  // the slot counters start at zero (a kernel, not a memset: callers may
+  // capture the stream in a graph)
+  hipLaunchKernelGGL(zero_i32, dim3(1), dim3(64), 0, stream, a.work_ctr, a.n_xcd);
+  hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, true, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+  return ok();
 }
 
 template <int D, int NQB, int NW, bool BOUND, bool MASK>
@@ -1234,12 +1352,37 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   a.gbits[0] = (uint32_t)gbits;
   a.gbits[1] = (uint32_t)(gbits >> 32);
 
+  if (blocks->work_ctr) {
+    if (!blocks->work_order) return fail(ATTN_E_INVAL, "work_ctr needs a work_order");
+    if (blocks->num_xcd < 1 || blocks->num_xcd > 32) return fail(ATTN_E_INVAL, "num_xcd must be in [1, 32]");
+    if (blocks->n_work % blocks->num_xcd) return fail(ATTN_E_INVAL, "n_work must be a multiple of num_xcd");
+  }
+  a.n_xcd = blocks->work_ctr ? blocks->num_xcd : 1;
+  a.work_ctr = blocks->work_ctr;
   const int grid = blocks->work_order ? blocks->n_work : (int)items;
   const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the kernels' query tile of 256 rows");
-  if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
+  // Bound path: persistent when a work_ctr is given (one workgroup per CU; a
+  // workgroup takes most of a CU's LDS), else one workgroup per item.
+  int cus = 0;
+  if (blocks->work_ctr && softmax_mode != ATTN_SOFTMAX_ONLINE) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return fail(ATTN_E_HIP, "cannot query the number of compute units");
+  }
+  if (cus > 0) {
+    const int pgrid = std::min(blocks->n_work, cus);
+    if (masked)
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, stream);
+    else
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream);
+    if (st) return st;
+  } else if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
     if (masked)
       st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
                            : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream);

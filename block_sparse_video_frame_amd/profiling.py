@@ -31,12 +31,17 @@ from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
-    m = re.search(r"fwd_kernel<([^>]*)>", kernel)
+    # fwd_kernel<D, NQB, NW, BOUND, MASK> (one workgroup per item) and
+    # fwd_persistent<D, NQB, NW, BOUND, MASK> (one per CU) compute the same
+    # items; both are reported under the path they run
+    m = re.search(r"fwd_(?:kernel|persistent)<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         path = "bound" if len(args) > 3 and args[3] == "true" else "online"
         masked = len(args) > 4 and args[4] == "true"
         return f"attn_fwd[{path}{',masked' if masked else ''}]"
+    if "zero_i32" in kernel:
+        return "attn_fwd[init]"
     m = re.search(r"prep_kernel<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BSVF_ABI_VERSION 1
+#define BSVF_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -210,6 +210,19 @@ typedef struct attn_blocks_t {
   const int32_t* work_order; /* device [n_work] from attn_build_schedule, or NULL
                                 for the natural order (one workgroup per item) */
   int32_t n_work;
+  int32_t num_xcd;           /* the num_xcd work_order was built with (1..32);
+                                read only when work_ctr is not NULL */
+  int32_t* work_ctr;         /* device int32 [num_xcd] workspace, or NULL.  Given
+                                (with a work_order), the bound path runs one
+                                workgroup per CU, each taking items from its
+                                accelerator die's queue of work_order and then
+                                from the others', counting handed-out slots
+                                here: dies that run faster take over the slower
+                                ones' work.  The online path keeps one workgroup
+                                per item.  The library zeroes it (stream-ordered)
+                                at the start of each call; calls that share it
+                                must not overlap.  NULL: one workgroup per item,
+                                in work_order's fixed order. */
 } attn_blocks_t;
 
 /*

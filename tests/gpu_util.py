@@ -23,9 +23,12 @@ def bf16_to_f64(t) -> np.ndarray:
     return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def run_gpu(q, k, v, pattern, scale, mode, block_q=256, schedule=True, layout="bhnd", repeat=1, granule=None):
+def run_gpu(q, k, v, pattern, scale, mode, block_q=256, schedule=True, layout="bhnd", repeat=1, granule=None,
+            persistent=True):
     """Runs norms + attention on the GPU; returns a dict of host arrays.  With
-    ``granule`` the block list is the frame-unaware one (masked kernel)."""
+    ``granule`` the block list is the frame-unaware one (masked kernel); with
+    ``schedule`` the launch follows build_schedule's order, taken item by item
+    by one workgroup per CU (``persistent``) or one workgroup per item."""
     import torch
     import block_sparse_video_frame_amd as bs
     B, H, N, D = q.shape
@@ -36,7 +39,7 @@ def run_gpu(q, k, v, pattern, scale, mode, block_q=256, schedule=True, layout="b
         qd, kd, vd = (to_device(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).permute(0, 2, 1, 3) for x in (q, k, v))
         out = torch.empty(B, N, H, D, dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
     host = bs.build_blocks_for(pattern, block_q) if granule is None else bs.build_blocks_granular(pattern, granule, block_q)
-    blk = host.to_device(torch.device("cuda"), B, H, schedule=schedule)
+    blk = host.to_device(torch.device("cuda"), B, H, schedule=schedule, persistent=persistent)
     nm = bs.norms(qd, kd) if mode != bs.SOFTMAX_ONLINE else None
     hp = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
     shift = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")

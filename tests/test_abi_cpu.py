@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     L = ctypes.CDLL(bs.library_path())
     for n in names:
         assert hasattr(L, n), n
-    assert bs.abi_version() == 1
+    hdr = open(HEADER).read()
+    assert bs.abi_version() == int(re.search(r"#define BSVF_ABI_VERSION (\d+)", hdr).group(1)) == bs.ABI_VERSION
     assert bs.lib().attn_status_str(3) == b"ATTN_E_PATTERN"
 
 
@@ -244,6 +245,10 @@ def fwd_call(**over):
     (dict(blocks={"n_qt": 0}), 1),
     (dict(blocks={"q_tiles": None}), 1),
     (dict(mode=1), 5),                 # bound mode without norms
+    (dict(blocks={"work_ctr": FAKE}), 1),                                   # counters without a work_order
+    (dict(blocks={"work_ctr": FAKE, "work_order": FAKE, "n_work": 16, "num_xcd": 0}), 1),
+    (dict(blocks={"work_ctr": FAKE, "work_order": FAKE, "n_work": 66, "num_xcd": 33}), 1),
+    (dict(blocks={"work_ctr": FAKE, "work_order": FAKE, "n_work": 12, "num_xcd": 8}), 1),  # not whole queues
     (dict(N=1 << 26, strides=[(1 << 26) * 64 * 2, (1 << 26) * 64, 64] * 4), 4),  # head span > 2^31
 ])
 def test_fwd_validation(over, status):

@@ -38,3 +38,13 @@ def test_committed_traffic_files_are_well_formed():
         assert 1.9 < d["fetch_scale"] < 2.1 and d["write_scale"] == 1.0
         assert "rocprofv3 --pmc FETCH_SIZE" in d["command_fetch"]
         assert "rocprofv3 --pmc WRITE_SIZE" in d["command_write"]
+
+
+def test_kernel_short_names():
+    from block_sparse_video_frame_amd.profiling import short_name
+    ns = "void bsvf::(anonymous namespace)::"
+    assert short_name(ns + "fwd_persistent<128, 1, 8, true, false>(bsvf::(anonymous namespace)::FwdArgs)") == "attn_fwd[bound]"
+    assert short_name(ns + "fwd_kernel<64, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
+        == "attn_fwd[online,masked]"
+    assert short_name(ns + "zero_i32(int*, int)") == "attn_fwd[init]"
+    assert short_name(ns + "head_max_kernel<true>(float const*, float const*, int, float*)") == "attn_norms[head_max]"
