@@ -161,10 +161,13 @@ class Blocks:
         def up(x):
             return torch.from_numpy(np.ascontiguousarray(x)).to(device)
 
+        persistent = persistent and order is not None
+        # slot counters of the persistent launch: zero once, left zero by every call
+        ctr = torch.zeros(num_xcd + 1, dtype=torch.int32, device=device) if persistent else None
         return DeviceBlocks(self, up(self.q_tiles), up(self.kv_ptr), up(self.kv_iv),
                             up(order) if order is not None else None, batch, heads,
                             up(self.kv_flag) if self.kv_flag is not None else None,
-                            num_xcd, persistent and order is not None)
+                            num_xcd, ctr)
 
 
 @dataclass
@@ -178,14 +181,17 @@ class DeviceBlocks:
     heads: int
     kv_flag: object = None
     num_xcd: int = 8
-    persistent: bool = False
+    # The persistent launch's slot counters (attn_blocks_t.work_ctr) or None.
+    # Calls that use the same DeviceBlocks must not overlap: one stream, or
+    # ordered by events.
+    work_ctr: object = None
 
-    def c_struct(self, work_ctr=None) -> _Blocks:
+    def c_struct(self) -> _Blocks:
         return _Blocks(self.q_tiles.data_ptr(), self.kv_ptr.data_ptr(), self.kv_iv.data_ptr(),
                        self.host.n_qt, self.host.nnz, self.host.block_q,
                        self.work_order.data_ptr() if self.work_order is not None else None,
                        int(self.work_order.numel()) if self.work_order is not None else 0,
-                       self.num_xcd, work_ctr.data_ptr() if work_ctr is not None else None)
+                       self.num_xcd, self.work_ctr.data_ptr() if self.work_ctr is not None else None)
 
 
 def build_blocks(num_frames: int, tokens_per_frame: int, win_before: int, win_after: int,
@@ -394,10 +400,7 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
     if lse is None:
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
-    # slot counters of the persistent launch, one set per call so that calls
-    # on different streams never share them (the library zeroes them)
-    ctr = torch.empty(blocks.num_xcd, dtype=torch.int32, device=q.device) if blocks.persistent else None
-    cb = blocks.c_struct(ctr)
+    cb = blocks.c_struct()
     qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
     so = shift_out.data_ptr() if shift_out is not None else None
     hp = head_path.data_ptr() if head_path is not None else None

@@ -89,7 +89,7 @@ struct FwdArgs {
   const int32_t* work_order;
   int32_t n_work;
   int32_t n_xcd;            // queues in work_order (persistent launch)
-  int32_t* work_ctr;        // their slot counters (persistent launch)
+  int32_t* work_ctr;        // their slot counters, then a done count (persistent launch)
   const float* q_norm;
   const float* k_gmax;
   const float* head_max;
@@ -1237,17 +1237,24 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
     run_item<D, NQB, NW, BOUND, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr, (const ci32*)ia.kv_iv,
                                       (const cf32*)ia.k_gmax, (const cf32*)ia.head_max, smem, w);
   }
+  // Leaving: work_ctr[n_xcd] counts the workgroups that are done.  The last
+  // one (every other workgroup has made its last slot request, as it counts
+  // itself only after them) sets all counters back to zero for the next call
+  // on this workspace.
+  if (threadIdx.x == 0) {
+    const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(args));
+    const kernarg_args& ka = *reinterpret_cast<const kernarg_args*>(args);
+    int32_t* counters = ka.work_ctr;
+    const int nx = ka.n_xcd;
+    if (atomicAdd(counters + nx, 1) == (int)gridDim.x - 1)
+      for (int x = 0; x <= nx; ++x) counters[x] = 0;
+  }
 }
 
-__global__ void zero_i32(int32_t* __restrict__ p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
-}
 
 template <int D, int NQB, int NW, bool MASK>
 int launch_persistent(const FwdArgs& a, int grid, hipStream_t stream) {
-  // the slot counters start at zero (a kernel, not a memset: callers may
-  // capture the stream in a graph)
-  hipLaunchKernelGGL(zero_i32, dim3(1), dim3(64), 0, stream, a.work_ctr, a.n_xcd);
   hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, true, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));

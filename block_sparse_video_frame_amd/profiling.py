@@ -40,8 +40,6 @@ def short_name(kernel: str) -> str:
         path = "bound" if len(args) > 3 and args[3] == "true" else "online"
         masked = len(args) > 4 and args[4] == "true"
         return f"attn_fwd[{path}{',masked' if masked else ''}]"
-    if "zero_i32" in kernel:
-        return "attn_fwd[init]"
     m = re.search(r"prep_kernel<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]

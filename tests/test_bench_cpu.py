@@ -46,5 +46,4 @@ def test_kernel_short_names():
     assert short_name(ns + "fwd_persistent<128, 1, 8, true, false>(bsvf::(anonymous namespace)::FwdArgs)") == "attn_fwd[bound]"
     assert short_name(ns + "fwd_kernel<64, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
         == "attn_fwd[online,masked]"
-    assert short_name(ns + "zero_i32(int*, int)") == "attn_fwd[init]"
     assert short_name(ns + "head_max_kernel<true>(float const*, float const*, int, float*)") == "attn_norms[head_max]"
