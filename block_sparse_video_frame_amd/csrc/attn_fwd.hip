@@ -10,12 +10,14 @@
 //     sum and accumulator whenever the max grows), or fixes each row's shift
 //     before the key loop to the Cauchy-Schwarz bound scale*|q_i|*max|k_j|
 //     from precomputed norms, so the loop never rescales; heads whose bound
-//     is too loose take the running-max path inside the same kernel.
+//     is too loose take the running-max path (here a second instantiation of
+//     the same kernel template, launched right after the first).
 //
 // gfx950 design (not the TPU kernel's):
-//   * One workgroup per query tile of up to 256 rows of one (batch, head):
-//     8 waves x 32 query rows.  A wave keeps its Q rows in VGPRs for the whole
-//     tile (the bound path keeps Q pre-multiplied by scale*log2(e)).
+//   * A workgroup computes one query tile of up to 256 rows of one (batch,
+//     head) at a time: 8 waves x 32 query rows.  A wave keeps its Q rows in
+//     VGPRs for the whole tile (the bound path keeps Q pre-multiplied by
+//     scale*log2(e)).
 //   * S^T = K * Q^T and O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16 (fp32
 //     accumulate).  With that orientation lane (n, h) of a 32x32 accumulator
 //     owns query n, so the row shift, the row sum and the rescale factor of a
@@ -35,6 +37,9 @@
 //     four waves, one per SIMD, hold the same 32 rows; each takes one 32-key
 //     half of every other stage, and the four merge their partial sums
 //     through LDS at the end.  Such a tile otherwise has one busy wave.
+//   * The bound path runs persistent: one workgroup per CU takes tiles from
+//     its accelerator die's queue of the launch order, then from the other
+//     dies' queues, since the dies do not run at equal speed.
 //   * exp is v_exp_f32 on base-2 scores; the tail stage zeroes the scores of
 //     missing 16-key groups (a per-group select, never a per-element mask).
 #include "bsvf_device.h"
@@ -278,12 +283,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
-// 16-byte LDS read that the compiler issues where it is written (volatile),
-// used to start operand reads several MFMAs ahead of their use.
-__device__ __forceinline__ bf16x8 lds_read_early(const u16* p) {
-  return *(const volatile lds_bf16x8*)(p);
-}
 
 // Transposing LDS read: within each 16-lane group, output lane i element j is
 // element i % 4 of the 8 bytes addressed by lane 4j + i / 4.
