@@ -464,38 +464,65 @@ struct Tile {
       kf[i] = k_operand(sm, boff, kbn(i), stn(i));
     float part[NQB][2];
     uint32_t pw[NQB][2][8];  // packed bf16 pairs: [qb][kb][r / 2]
+    // The softmax of chunk i is skewed over three chunks -- its exps in chunk
+    // i, their conversion to bf16 in chunk i+1, the row-sum update in chunk
+    // i+2 -- so no instruction waits on a result issued just before it; the
+    // wave's matrix and vector work then interleave without stalls.  The
+    // order of the row-sum updates, and so every bit, is unchanged.
+    float pe[NM][NQB][EPM];        // chunk i's probabilities (fp32)
+    uint32_t pp[NM][NQB][EPM / 2];  // chunk i's packed bf16 pairs
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) part[qb][0] = part[qb][1] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i + AHEAD < NM) {
-        const int j = i + AHEAD;
-        kf[j] = k_operand(sm, boff, kbn(j), stn(j));
-      }
-      if (i == C::KSTEPS) {
+    for (int i = 0; i < NM + 2; ++i) {
+      if (i < NM) {
+        if (i + AHEAD < NM) {
+          const int j = i + AHEAD;
+          kf[j] = k_operand(sm, boff, kbn(j), stn(j));
+        }
+        if (i == C::KSTEPS) {
+#pragma unroll
+          for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) nxt[0][qb][r] = acc0(qb);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb)
+          nxt[kbn(i)][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[qb][stn(i)], nxt[kbn(i)][qb], 0, 0, 0);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) nxt[0][qb][r] = acc0(qb);
+          for (int e = 0; e < EPM; ++e) {
+            const int el = i * EPM + e, kb = el >> 4, r = el & 15;
+            pe[i][qb][e] = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r] : fmaf(cur[kb][qb][r], c2, nm[qb]));
+            // keep this slice here: without a use at this point the
+            // compiler sinks the whole softmax below the MFMAs
+            asm volatile("" : "+v"(pe[i][qb][e]));
+          }
       }
+      if (i >= 1 && i <= NM) {
+        const int c = i - 1;
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-        nxt[kbn(i)][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[qb][stn(i)], nxt[kbn(i)][qb], 0, 0, 0);
+        for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+          for (int e = 0; e < EPM; e += 2) {
+            const int el = c * EPM + e, kb = el >> 4, r = el & 15;
+            f32x2 f = {pe[c][qb][e], pe[c][qb][e + 1]};
+            uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+            asm volatile("" : "+v"(w));
+            pp[c][qb][e >> 1] = w;
+            pw[qb][kb][r >> 1] = w;
+          }
+      }
+      if (i >= 2) {
+        const int c = i - 2;
 #pragma unroll
-        for (int e = 0; e < EPM; e += 2) {
-          const int el = i * EPM + e, kb = el >> 4, r = el & 15;
-          const float p0 = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r] : fmaf(cur[kb][qb][r], c2, nm[qb]));
-          const float p1 = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r + 1] : fmaf(cur[kb][qb][r + 1], c2, nm[qb]));
-          f32x2 f = {p0, p1};
-          const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-          pw[qb][kb][r >> 1] = w;
-          part[qb][(e >> 1) & 1] = add_pair(w, part[qb][(e >> 1) & 1]);
-          // keep this slice here: without a use at this point the compiler
-          // sinks the whole softmax below the MFMAs
-          asm volatile("" : "+v"(part[qb][0]), "+v"(part[qb][1]), "+v"(pw[qb][kb][r >> 1]));
+        for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+          for (int e = 0; e < EPM; e += 2) part[qb][(e >> 1) & 1] = add_pair(pp[c][qb][e >> 1], part[qb][(e >> 1) & 1]);
+          asm volatile("" : "+v"(part[qb][0]), "+v"(part[qb][1]));
         }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
