@@ -317,7 +317,8 @@ struct Tile {
   bf16x8 qreg[NQB][C::KSTEPS];
   f32x16 oacc[NQB][C::DBLK];
   float m2[NQB];    // row shift in log2 units (bound: fixed; online: running max)
-  float lsum[NQB];  // this lane half's share of the row sum
+  float lsum[NQB];   // this lane half's share of the row sum
+  float lsum2[NQB];  // a second running sum, fed where a chunk holds two pairs (D = 64)
   int n, hh, lane;
   int fq[NQB];  // frame of this lane's query row (frame-unaware layout only)
   LaneOffsets<D> lof;
@@ -379,6 +380,7 @@ struct Tile {
         alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - msafe);
         m2[qb] = mnew;
         lsum[qb] *= alpha[qb];
+        lsum2[qb] *= alpha[qb];
       }
       const float nm = m2[qb] == -INFINITY ? 0.0f : -m2[qb];
       float p[2][16];
@@ -443,6 +445,7 @@ struct Tile {
         alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - msafe);
         m2[qb] = mnew;
         lsum[qb] *= alpha[qb];
+        if constexpr (EPM > 2) lsum2[qb] *= alpha[qb];
       }
       nm[qb] = m2[qb] == -INFINITY ? 0.0f : -m2[qb];
     }
@@ -462,17 +465,15 @@ struct Tile {
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i)
       kf[i] = k_operand(sm, boff, kbn(i), stn(i));
-    float part[NQB][2];
     uint32_t pw[NQB][2][8];  // packed bf16 pairs: [qb][kb][r / 2]
     // The softmax of chunk i is skewed over three chunks -- its exps in chunk
     // i, their conversion to bf16 in chunk i+1, the row-sum update in chunk
     // i+2 -- so no instruction waits on a result issued just before it; the
-    // wave's matrix and vector work then interleave without stalls.  The
-    // order of the row-sum updates, and so every bit, is unchanged.
+    // wave's matrix and vector work then interleave without stalls.  Pairs
+    // go straight into the running row sums (the second one where a chunk
+    // holds two pairs), with no per-stage partial sums to start and fold.
     float pe[NM][NQB][EPM];        // chunk i's probabilities (fp32)
     uint32_t pp[NM][NQB][EPM / 2];  // chunk i's packed bf16 pairs
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) part[qb][0] = part[qb][1] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NM + 2; ++i) {
       if (i < NM) {
@@ -519,15 +520,17 @@ struct Tile {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
-          for (int e = 0; e < EPM; e += 2) part[qb][(e >> 1) & 1] = add_pair(pp[c][qb][e >> 1], part[qb][(e >> 1) & 1]);
-          asm volatile("" : "+v"(part[qb][0]), "+v"(part[qb][1]));
+          for (int e = 0; e < EPM; e += 2) {
+            if ((e >> 1) & 1) lsum2[qb] = add_pair(pp[c][qb][e >> 1], lsum2[qb]);
+            else lsum[qb] = add_pair(pp[c][qb][e >> 1], lsum[qb]);
+          }
+          asm volatile("" : "+v"(lsum[qb]), "+v"(lsum2[qb]));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
-      lsum[qb] += part[qb][0] + part[qb][1];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1116,6 +1119,7 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
       T.m2[qb] = -INFINITY;
     }
     T.lsum[qb] = 0.0f;
+    T.lsum2[qb] = 0.0f;
 #pragma unroll
     for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -1146,7 +1150,8 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
   u16* oh = a.o + b * a.so[0] + h * a.so[1];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
-    const float lt = T.lsum[qb] + __shfl_xor(T.lsum[qb], 32);
+    const float lh = T.lsum[qb] + T.lsum2[qb];
+    const float lt = lh + __shfl_xor(lh, 32);
     const int r = row0 + qb * 32 + T.n;
     if (r >= nr) continue;
     const float inv = 1.0f / lt;
