@@ -390,3 +390,22 @@ def test_granular_builder_errors():
         bs.build_blocks_granular(p, 96, 128)      # granule not a multiple of 64
     with pytest.raises(bs.AttnError):
         bs.build_blocks_granular(p, 128, 40)      # block_q not a multiple of 16
+
+
+def test_device_blocks_workspace():
+    """The device block list carries the persistent launch's counters: zeroed,
+    num_xcd + 1 of them, passed through attn_blocks_t; none for a static launch."""
+    import torch
+    blk = bs.build_blocks_for(Pattern(2, 32, 1, 1), 32)
+    cpu = torch.device("cpu")
+    d = blk.to_device(cpu, 1, 2, num_xcd=8)
+    assert d.work_ctr is not None and d.work_ctr.dtype == torch.int32
+    assert d.work_ctr.numel() == 9 and not d.work_ctr.any()
+    cs = d.c_struct()
+    assert cs.num_xcd == 8 and cs.work_ctr == d.work_ctr.data_ptr()
+    assert cs.work_order == d.work_order.data_ptr() and cs.n_work == d.work_order.numel()
+    assert d.work_order.numel() % 8 == 0
+    assert blk.to_device(cpu, 1, 2, persistent=False).work_ctr is None
+    assert blk.to_device(cpu, 1, 2, persistent=False).c_struct().work_ctr is None
+    assert blk.to_device(cpu, 1, 2, schedule=False).work_ctr is None
+    assert blk.to_device(cpu, 1, 2, num_xcd=3).work_ctr.numel() == 4
