@@ -1216,6 +1216,7 @@ typedef __attribute__((address_space(4))) const FwdArgs kernarg_args;
 // for both paths would need more registers than the bound path alone.)
 template <int D, int NQB, int NW, bool BOUND, bool MASK>
 __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
+  (void)a;  // read through the argument-segment pointer below
   using C = Cfg<D, NQB, NW>;
   __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
   uint32_t empty = 0;  // thread 0: the queues found exhausted
@@ -1278,8 +1279,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
     const kernarg_args& ka = *reinterpret_cast<const kernarg_args*>(args);
     int32_t* counters = ka.work_ctr;
     const int nx = ka.n_xcd;
+    // (atomic writes: the next call's slot requests may come from other dies)
     if (atomicAdd(counters + nx, 1) == (int)gridDim.x - 1)
-      for (int x = 0; x <= nx; ++x) counters[x] = 0;
+      for (int x = 0; x <= nx; ++x) atomicExch(counters + x, 0);
   }
 }
 
