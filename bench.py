@@ -175,7 +175,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="720p")
-    ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with fallback, 2 forced bound")
+    ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with per-head fallback, 2 forced bound, 3 bound per query tile")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", default="aligned16", choices=["aligned16", "granular128"],
@@ -286,7 +286,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name} chunk: B{B} H{H} D{D}, {wl.pattern.num_frames} frames x "
                                f"{wl.pattern.tokens_per_frame} tokens (N {N}), window -{wl.pattern.win_before}/"
-                               f"+{wl.pattern.win_after}, global {list(wl.pattern.global_frames)}",
+                               f"+{wl.pattern.win_after}, global {list(wl.pattern.global_frames)}"
+                               + (f", Q and K rows of frame {wl.hot_frame[0]} x{wl.hot_frame[1]:g}" if wl.hot_frame else ""),
                    "softmax_mode": args.mode, "block_q": bs.MAX_BLOCK_Q, "layout": args.layout,
                    "useful_flop": useful_flop, "useful_pairs_per_head": blocks.useful_pairs},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

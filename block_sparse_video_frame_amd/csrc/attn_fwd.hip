@@ -1203,6 +1203,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
 typedef __attribute__((address_space(4))) const char kernarg_char;
 typedef __attribute__((address_space(4))) const FwdArgs kernarg_args;
 
+// A copy of the kernel arguments read through a pointer to the argument
+// segment that the compiler cannot see through, so that two copies are two
+// sets of loads rather than one set of values kept live between them.
+// (`a`, the only kernel argument of fwd_persistent, starts the segment.)
+__device__ __forceinline__ void item_args(FwdArgs& ia) {
+  const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(args));
+  static_assert(sizeof(FwdArgs) % 4 == 0, "FwdArgs is copied in dwords");
+  typedef __attribute__((address_space(4))) const uint32_t kernarg_u32;
+  const kernarg_u32* src = (const kernarg_u32*)args;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&ia);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(FwdArgs) / 4); ++i) dst[i] = src[i];
+}
+
 // Persistent launch: one workgroup per CU, each taking items until none is
 // left.  work_order holds n_xcd queues (slot j of queue x at j * n_xcd + x,
 // padding -1 only at a queue's end); work_ctr[x] counts the slots of queue x
@@ -1210,11 +1225,13 @@ typedef __attribute__((address_space(4))) const FwdArgs kernarg_args;
 // die (XCC) first -- the schedule keeps the tiles of one frame, which read
 // the same keys, in one queue -- and then from the others, so a die that runs
 // faster takes over work a slower one has not reached instead of idling
-// while it finishes.  It computes the items on the path BOUND and passes
-// over the others (the static launch of the other path takes those); the
-// outputs do not depend on which workgroup computes an item.  (One kernel
-// for both paths would need more registers than the bound path alone.)
-template <int D, int NQB, int NW, bool BOUND, bool MASK>
+// while it finishes.  Each item runs on its own softmax path in the same
+// queue: the bound path's code takes it first and declines it, having
+// written nothing, when the item takes the online path, which then runs it.
+// So online items (whole heads in mode 1, single tiles in mode 3) fill the
+// same CUs as the bound ones instead of following them in a launch of their
+// own.  The outputs do not depend on which workgroup computes an item.
+template <int D, int NQB, int NW, bool MASK>
 __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   (void)a;  // read through the argument-segment pointer below
   using C = Cfg<D, NQB, NW>;
@@ -1253,21 +1270,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(word[0]);
     __syncthreads();  // read by every wave before the item's copies reuse it
     if (w < 0) break;
-    // The item reads its arguments through the same opaque pointer, so none
-    // is held in a scalar register from one item to the next.
-    const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(args));
+    // Each path reads the item's arguments afresh through the opaque
+    // pointer, so none is held in a scalar register from one item, or one
+    // path, to the next.  (a declined item has finished with the LDS it
+    // used: see run_item)
     FwdArgs ia;
-    static_assert(sizeof(FwdArgs) % 4 == 0, "FwdArgs is copied in dwords");
-    {
-      typedef __attribute__((address_space(4))) const uint32_t kernarg_u32;
-      const kernarg_u32* src = (const kernarg_u32*)args;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&ia);
-#pragma unroll
-      for (int i = 0; i < (int)(sizeof(FwdArgs) / 4); ++i) dst[i] = src[i];
+    item_args(ia);
+    if (!run_item<D, NQB, NW, true, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr,
+                                          (const ci32*)ia.kv_iv, (const cf32*)ia.k_gmax,
+                                          (const cf32*)ia.head_max, smem, w)) {
+      FwdArgs ib;
+      item_args(ib);
+      run_item<D, NQB, NW, false, MASK>(ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr,
+                                        (const ci32*)ib.kv_iv, (const cf32*)ib.k_gmax,
+                                        (const cf32*)ib.head_max, smem, w);
     }
-    run_item<D, NQB, NW, BOUND, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr, (const ci32*)ia.kv_iv,
-                                      (const cf32*)ia.k_gmax, (const cf32*)ia.head_max, smem, w);
   }
   // Leaving: work_ctr[n_xcd] counts the workgroups that are done.  The last
   // one (every other workgroup has made its last slot request, as it counts
@@ -1286,9 +1303,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
 }
 
 
+static_assert(ONLINE_NQB == BOUND_NQB && ONLINE_NW == BOUND_NW,
+              "the persistent kernel runs both paths on one tile shape");
+
 template <int D, int NQB, int NW, bool MASK>
 int launch_persistent(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, true, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return ok();
@@ -1404,8 +1424,11 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the kernels' query tile of 256 rows");
-  // Bound path: persistent when a work_ctr is given (one workgroup per CU; a
-  // workgroup takes most of a CU's LDS), else one workgroup per item.
+  // With a work_ctr, modes that can take the bound path run every item on
+  // its path in one persistent launch (one workgroup per CU; a workgroup
+  // takes most of a CU's LDS).  Otherwise each path has a launch of one
+  // workgroup per item; the online mode keeps that launch, which measured 1-2%
+  // faster than the persistent one for it.
   int cus = 0;
   if (blocks->work_ctr && softmax_mode != ATTN_SOFTMAX_ONLINE) {
     int dev = 0;
@@ -1421,8 +1444,9 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
     else
       st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream)
                            : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream);
-    if (st) return st;
-  } else if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
+    return st ? st : ok();
+  }
+  if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
     if (masked)
       st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
                            : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream);

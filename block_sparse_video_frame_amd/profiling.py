@@ -31,10 +31,16 @@ from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
-    # fwd_kernel<D, NQB, NW, BOUND, MASK> (one workgroup per item) and
-    # fwd_persistent<D, NQB, NW, BOUND, MASK> (one per CU) compute the same
-    # items; both are reported under the path they run
-    m = re.search(r"fwd_(?:kernel|persistent)<([^>]*)>", kernel)
+    # fwd_persistent<D, NQB, NW, MASK>: one workgroup per CU, each item on
+    # its own softmax path
+    m = re.search(r"fwd_persistent<([^>]*)>", kernel)
+    if m:
+        args = [x.strip() for x in m.group(1).split(",")]
+        masked = len(args) > 3 and args[3] == "true"
+        return f"attn_fwd[persistent{',masked' if masked else ''}]"
+    # fwd_kernel<D, NQB, NW, BOUND, MASK>: one workgroup per item, reported
+    # under the path it runs
+    m = re.search(r"fwd_kernel<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         path = "bound" if len(args) > 3 and args[3] == "true" else "online"
@@ -90,7 +96,7 @@ def counters(directory: str):
 
 def traffic(fetch_dir: str, write_dir: str, copy_bytes: float, kernel: str = "attn_fwd"):
     """HBM bytes per call of ``kernel`` (all kernels whose short name starts
-    with it: attn_fwd's bound and online instantiations, say)."""
+    with it: every launch of one attn_fwd call, say)."""
     fc = counters(fetch_dir)
     wc = counters(write_dir)
     # the calibration copy is by far the largest copy dispatch of the run

@@ -14,6 +14,7 @@ tiny       1       2      64    4 x 48   (N 192)    +-1 frame
 720p       1       8      128   13 x 3600 (N 46800) +-1 frame + frame 0 global
 1080p      1       8      128   7 x 8160 (N 57120)  +-1 frame + frame 0 global
 stress     as 720p, rows scaled by log-normal(0, 0.75) norms, 1% of keys x8
+hotframe   as 720p, the Q and K rows of frame 6 doubled
 sr         1       16     64    5 x 14400 (N 72000) frame-local
 =========  ======  =====  ====  ==================  ==========================
 
@@ -23,7 +24,10 @@ round-to-nearest-even on the bit pattern.  The stress workload draws the same
 Q, K, V first, then ``z_q``, ``z_k`` (``[B, H, N]`` standard normal) and an
 outlier uniform ``[B, H, N]``; each Q row is multiplied by ``exp(0.75 z_q)``,
 each K row by ``exp(0.75 z_k)`` and, where the uniform is below 0.01, by 8;
-all in float32, rounded to bf16 once at the end.  V is left unscaled.
+all in float32, rounded to bf16 once at the end.  V is left unscaled.  The
+hotframe workload takes the 720p Q and K and doubles every row of frame 6
+(exact in bf16): per-head eligibility then fails on every head, while the
+tiles whose keys avoid frame 6 stay eligible.
 
 The Q/K producer (per-head RMS norm, then rotary embedding) takes the same
 Q and K as its pre-norm input, RMS-norm weights from ``norm_weights`` and
@@ -65,6 +69,7 @@ class Workload:
     pattern: Pattern
     stress: bool = False
     seed: int = 0
+    hot_frame: tuple = ()   # (frame, factor): Q and K rows of that frame scaled
 
     @property
     def seq_len(self) -> int:
@@ -82,6 +87,7 @@ WORKLOADS = {
     "1080p": Workload("1080p", 1, 8, 128, Pattern(7, 8160, 1, 1, (0,))),
     "stress": Workload("stress", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), stress=True),
     "sr": Workload("sr", 1, 16, 64, Pattern(5, 14400, 0, 0)),
+    "hotframe": Workload("hotframe", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), hot_frame=(6, 2.0)),
 }
 
 
@@ -93,6 +99,7 @@ FRAME_GRID = {
     "1080p": (68, 120),
     "stress": (45, 80),
     "sr": (90, 160),
+    "hotframe": (45, 80),
 }
 
 
@@ -146,8 +153,16 @@ def random_qkv(batch, heads, seq_len, head_dim, seed=0, stress=False, stress_par
 
 def make_qkv(wl: Workload, seed: int | None = None):
     """Q, K, V bf16 bit arrays for a named workload."""
-    return random_qkv(wl.batch, wl.heads, wl.seq_len, wl.head_dim,
-                      wl.seed if seed is None else seed, wl.stress)
+    q, k, v = random_qkv(wl.batch, wl.heads, wl.seq_len, wl.head_dim,
+                         wl.seed if seed is None else seed, wl.stress)
+    if wl.hot_frame:
+        f, c = wl.hot_frame
+        T = wl.pattern.tokens_per_frame
+        q, k = (x.copy() for x in (q, k))
+        for x in (q, k):
+            rows = bf16_bits_to_f32(x[:, :, f * T:(f + 1) * T]) * np.float32(c)
+            x[:, :, f * T:(f + 1) * T] = f32_to_bf16_bits(rows)
+    return q, k, v
 
 
 def sha256(a: np.ndarray) -> str:
