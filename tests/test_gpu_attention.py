@@ -167,7 +167,7 @@ def test_online_and_bound_agree():
     assert within(e), e
 
 
-@pytest.mark.parametrize("name", ["1080p", "720p"])
+@pytest.mark.parametrize("name", ["1080p", "720p", "hotframe"])
 def test_launch_order_does_not_change_results(name):
     """The persistent launch (items taken dynamically from per-die queues),
     the static launch in the same order and the natural order give the same
@@ -366,6 +366,43 @@ def test_hot_frame_workload(mode):
         assert (on_bound == elig[:, :, tile_of]).all()
         b_ = elig[:, :, tile_of]
         assert (np.abs(shift - bd * (1 + 2.0 ** -8))[b_] <= 1e-5 * np.maximum(bd[b_], 1)).all()
+
+
+def _mixed_head_inputs():
+    """Four heads of N(0,1) bf16 inputs; heads 1 and 3 have every Q and K row
+    doubled (exact in bf16), which fails the per-head test."""
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    p = Pattern(5, 304, 1, 1, (0,))
+    B, H, D = 1, 4, 128
+    q, k, v = random_qkv(B, H, p.seq_len, D, seed=41)
+    q, k = q.copy(), k.copy()
+    for x in (q, k):
+        x[:, 1::2] = f32_to_bf16_bits(bf16_bits_to_f32(x[:, 1::2]) * np.float32(2.0))
+    return p, D, q, k, v
+
+
+def test_mixed_head_paths_in_one_call():
+    """Mode 1 with heads on both paths in one call: each head takes the path
+    the oracle's per-head test gives, the results match the oracle, and the
+    persistent launch (both paths from one queue) gives the bits of the
+    static launches (one per path)."""
+    p, D, q, k, v = _mixed_head_inputs()
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    hm = ON.head_max(ON.row_norms(q), ON.row_norms(k))
+    sl = ON.slack_bound(hm, scale)
+    assert (np.abs(sl - ON.ELIGIBLE_NATS) > 1e-3 * ON.ELIGIBLE_NATS).all()
+    want = ON.eligible(hm, scale).astype(np.int32)
+    assert (want == np.array([[1, 0, 1, 0]])).all()
+    O, L = OA.attention(q, k, v, p, scale)
+    # the doubled heads attend sharply (|O| above 1): band scaled by max(1, |O_ref|)
+    s = np.maximum(1.0, np.abs(O))
+    a = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND)
+    b = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND, persistent=False)
+    for r in (a, b):
+        assert (r["head_path"] == want).all(), r["head_path"]
+        e = errors(r["o"] / s, r["lse"], O / s, L)
+        assert within(e), e
+    assert a["o_bytes"] == b["o_bytes"] and a["lse_bytes"] == b["lse_bytes"]
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
