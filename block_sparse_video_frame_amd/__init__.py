@@ -152,11 +152,10 @@ class Blocks:
     def to_device(self, device, batch: int, heads: int, schedule: bool = True, group: int = 0,
                   num_xcd: int = 8, persistent: bool = True) -> "DeviceBlocks":
         """Device copy of the list.  With ``schedule`` the launch order comes from
-        :func:`build_schedule`; with ``persistent`` as well, attention in the
-        modes that can take the bound path runs one workgroup per CU taking
-        items from the order's per-die queues, each item on its own softmax
-        path (see ``attn_blocks_t.work_ctr``); otherwise one workgroup per
-        item."""
+        :func:`build_schedule`; with ``persistent`` as well, attention runs
+        one workgroup per CU taking items from the order's per-die queues,
+        each item on its own softmax path (see ``attn_blocks_t.work_ctr``);
+        otherwise one workgroup per item."""
         import torch
         order = build_schedule(self, batch, heads, group, num_xcd) if schedule else None
 

@@ -1225,13 +1225,15 @@ __device__ __forceinline__ void item_args(FwdArgs& ia) {
 // die (XCC) first -- the schedule keeps the tiles of one frame, which read
 // the same keys, in one queue -- and then from the others, so a die that runs
 // faster takes over work a slower one has not reached instead of idling
-// while it finishes.  Each item runs on its own softmax path in the same
-// queue: the bound path's code takes it first and declines it, having
-// written nothing, when the item takes the online path, which then runs it.
-// So online items (whole heads in mode 1, single tiles in mode 3) fill the
-// same CUs as the bound ones instead of following them in a launch of their
-// own.  The outputs do not depend on which workgroup computes an item.
-template <int D, int NQB, int NW, bool MASK>
+// while it finishes.  With BOTH, each item runs on its own softmax path in
+// the same queue: the bound path's code takes it first and declines it,
+// having written nothing, when the item takes the online path, which then
+// runs it.  So online items (whole heads in mode 1, single tiles in mode 3)
+// fill the same CUs as the bound ones instead of following them in a launch
+// of their own.  Without BOTH the kernel holds the online path alone (the
+// online mode): sharing a kernel with the bound path costs the online loop
+// about 2%.  The outputs do not depend on which workgroup computes an item.
+template <int D, int NQB, int NW, bool MASK, bool BOTH>
 __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   (void)a;  // read through the argument-segment pointer below
   using C = Cfg<D, NQB, NW>;
@@ -1274,11 +1276,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
     // pointer, so none is held in a scalar register from one item, or one
     // path, to the next.  (a declined item has finished with the LDS it
     // used: see run_item)
-    FwdArgs ia;
-    item_args(ia);
-    if (!run_item<D, NQB, NW, true, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr,
-                                          (const ci32*)ia.kv_iv, (const cf32*)ia.k_gmax,
-                                          (const cf32*)ia.head_max, smem, w)) {
+    bool done = false;
+    if constexpr (BOTH) {
+      FwdArgs ia;
+      item_args(ia);
+      done = run_item<D, NQB, NW, true, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr,
+                                              (const ci32*)ia.kv_iv, (const cf32*)ia.k_gmax,
+                                              (const cf32*)ia.head_max, smem, w);
+    }
+    if (!done) {
       FwdArgs ib;
       item_args(ib);
       run_item<D, NQB, NW, false, MASK>(ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr,
@@ -1307,8 +1313,9 @@ static_assert(ONLINE_NQB == BOUND_NQB && ONLINE_NW == BOUND_NW,
               "the persistent kernel runs both paths on one tile shape");
 
 template <int D, int NQB, int NW, bool MASK>
-int launch_persistent(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a);
+int launch_persistent(const FwdArgs& a, int grid, bool both, hipStream_t stream) {
+  if (both) hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return ok();
@@ -1424,13 +1431,12 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the kernels' query tile of 256 rows");
-  // With a work_ctr, modes that can take the bound path run every item on
-  // its path in one persistent launch (one workgroup per CU; a workgroup
-  // takes most of a CU's LDS).  Otherwise each path has a launch of one
-  // workgroup per item; the online mode keeps that launch, which measured 1-2%
-  // faster than the persistent one for it.
+  // With a work_ctr, one persistent launch runs every item on its path (one
+  // workgroup per CU; a workgroup takes most of a CU's LDS); in the online
+  // mode its kernel holds the online path only.  Without one, each path has
+  // a launch of one workgroup per item.
   int cus = 0;
-  if (blocks->work_ctr && softmax_mode != ATTN_SOFTMAX_ONLINE) {
+  if (blocks->work_ctr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
@@ -1438,12 +1444,13 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   }
   if (cus > 0) {
     const int pgrid = std::min(blocks->n_work, cus);
+    const bool both = softmax_mode != ATTN_SOFTMAX_ONLINE;
     if (masked)
-      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, stream)
-                           : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, stream);
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream);
     else
-      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream)
-                           : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, stream);
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, stream);
     return st ? st : ok();
   }
   if (softmax_mode != ATTN_SOFTMAX_ONLINE) {

@@ -31,13 +31,14 @@ from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
-    # fwd_persistent<D, NQB, NW, MASK>: one workgroup per CU, each item on
-    # its own softmax path
+    # fwd_persistent<D, NQB, NW, MASK, BOTH>: one workgroup per CU, each item
+    # on its own softmax path (BOTH), or the online path alone
     m = re.search(r"fwd_persistent<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         masked = len(args) > 3 and args[3] == "true"
-        return f"attn_fwd[persistent{',masked' if masked else ''}]"
+        online = len(args) > 4 and args[4] == "false"
+        return f"attn_fwd[persistent{',online' if online else ''}{',masked' if masked else ''}]"
     # fwd_kernel<D, NQB, NW, BOUND, MASK>: one workgroup per item, reported
     # under the path it runs
     m = re.search(r"fwd_kernel<([^>]*)>", kernel)

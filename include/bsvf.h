@@ -213,16 +213,14 @@ typedef struct attn_blocks_t {
   int32_t num_xcd;           /* the num_xcd work_order was built with (1..32);
                                 read only when work_ctr is not NULL */
   int32_t* work_ctr;         /* device int32 [num_xcd + 1] workspace, or NULL.
-                                Given (with a work_order) and softmax_mode not
-                                ATTN_SOFTMAX_ONLINE, one launch runs every item
-                                on its own path (bound or online), one workgroup
-                                per CU, each taking items from its accelerator
-                                die's queue of work_order and then from the
-                                others', counting handed-out slots here: dies
-                                that run faster take over the slower ones' work,
-                                and online items share the CUs with bound ones.
-                                ATTN_SOFTMAX_ONLINE keeps one workgroup per
-                                item.  The caller zeroes it once before its
+                                Given (with a work_order), one launch runs
+                                every item on its own path (bound or online),
+                                one workgroup per CU, each taking items from its
+                                accelerator die's queue of work_order and then
+                                from the others', counting handed-out slots
+                                here: dies that run faster take over the slower
+                                ones' work, and online items share the CUs with
+                                bound ones.  The caller zeroes it once before its
                                 first use; every call leaves it zero again.
                                 Calls that share it must not overlap (one
                                 stream, or ordered by events).  NULL: one

@@ -43,9 +43,12 @@ def test_committed_traffic_files_are_well_formed():
 def test_kernel_short_names():
     from block_sparse_video_frame_amd.profiling import short_name
     ns = "void bsvf::(anonymous namespace)::"
-    assert short_name(ns + "fwd_persistent<128, 1, 8, false>(bsvf::(anonymous namespace)::FwdArgs)") == "attn_fwd[persistent]"
-    assert short_name(ns + "fwd_persistent<64, 1, 8, true>(bsvf::(anonymous namespace)::FwdArgs)") \
+    assert short_name(ns + "fwd_persistent<128, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[persistent]"
+    assert short_name(ns + "fwd_persistent<64, 1, 8, true, true>(bsvf::(anonymous namespace)::FwdArgs)") \
         == "attn_fwd[persistent,masked]"
+    assert short_name(ns + "fwd_persistent<128, 1, 8, false, false>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[persistent,online]"
     assert short_name(ns + "fwd_kernel<128, 1, 8, true, false>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
         == "attn_fwd[bound]"
     assert short_name(ns + "fwd_kernel<64, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \

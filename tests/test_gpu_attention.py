@@ -468,23 +468,25 @@ def test_random_patterns_all_rows(case):
             assert within(e), (p, D, bq, mode, "granular", e)
 
 
+@pytest.mark.parametrize("mode", [bs.SOFTMAX_BOUND, bs.SOFTMAX_ONLINE])
 @pytest.mark.parametrize("num_xcd,group", [(1, 0), (3, 0), (16, 0), (8, 32)])
-def test_persistent_launch_any_queue_layout(num_xcd, group):
-    """The persistent launch takes its die's queue modulo the queue count, so
-    any num_xcd (and the group-dealt order) gives the natural order's bits;
-    two calls in a row check that each call leaves the counters at zero."""
+def test_persistent_launch_any_queue_layout(num_xcd, group, mode):
+    """The persistent launch (both paths, or the online path alone) takes its
+    die's queue modulo the queue count, so any num_xcd (and the group-dealt
+    order) gives the natural order's bits; two calls in a row check that each
+    call leaves the counters at zero."""
     import torch
     p, B, H, D = Pattern(5, 304, 1, 1, (0,)), 1, 3, 128
     q, k, v = random_qkv(B, H, p.seq_len, D, seed=11)
     scale = 1.0 / math.sqrt(D)
-    ref = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND, schedule=False)
+    ref = run_gpu(q, k, v, p, scale, mode, schedule=False)
     from gpu_util import to_device
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     blk = bs.build_blocks_for(p, 256).to_device(torch.device("cuda"), B, H, group=group, num_xcd=num_xcd)
     assert blk.work_ctr is not None and blk.work_ctr.numel() == num_xcd + 1
     nm = bs.norms(qd, kd)
     for _ in range(2):
-        o, lse = bs.attention(qd, kd, vd, blk, scale, bs.SOFTMAX_BOUND, norms=nm)
+        o, lse = bs.attention(qd, kd, vd, blk, scale, mode, norms=nm if mode != bs.SOFTMAX_ONLINE else None)
         torch.cuda.synchronize()
         assert o.contiguous().view(torch.int16).cpu().numpy().tobytes() == ref["o_bytes"]
         assert lse.cpu().numpy().tobytes() == ref["lse_bytes"]
