@@ -226,3 +226,24 @@ def test_tile_slack_bound_pins():
     whole = NM.tile_slack_bound(q, k, Pattern(3, 32, 2, 2), scale, [(0, 96)])
     head2 = NM.slack_bound(NM.head_max(NM.row_norms(q), NM.row_norms(k)), scale)
     assert np.allclose(whole[..., 0], head2, rtol=1e-14)
+
+
+def test_hot_frame_recipe():
+    """The hotframe input is the 720p input with the Q and K rows of frame 6
+    doubled, exactly (a power of two in bf16), and nothing else changed; shown
+    on a small pattern with the same recipe."""
+    import dataclasses
+    from synth import WORKLOADS, Workload, bf16_bits_to_f32, make_qkv
+    hot = WORKLOADS["hotframe"]
+    assert dataclasses.replace(hot, name="720p", hot_frame=()) == WORKLOADS["720p"]
+    assert hot.hot_frame == (6, 2.0)
+    p = Pattern(8, 48, 1, 1, (0,))
+    base = Workload("small", 1, 2, 64, p)
+    q0, k0, v0 = make_qkv(base)
+    q1, k1, v1 = make_qkv(dataclasses.replace(base, hot_frame=(6, 2.0)))
+    T = p.tokens_per_frame
+    rows = slice(6 * T, 7 * T)
+    for a, b in ((q0, q1), (k0, k1)):
+        assert np.array_equal(bf16_bits_to_f32(b[:, :, rows]), 2.0 * bf16_bits_to_f32(a[:, :, rows]))
+        assert np.array_equal(np.delete(a, np.s_[6 * T:7 * T], axis=2), np.delete(b, np.s_[6 * T:7 * T], axis=2))
+    assert np.array_equal(v0, v1)
