@@ -247,3 +247,36 @@ def test_hot_frame_recipe():
         assert np.array_equal(bf16_bits_to_f32(b[:, :, rows]), 2.0 * bf16_bits_to_f32(a[:, :, rows]))
         assert np.array_equal(np.delete(a, np.s_[6 * T:7 * T], axis=2), np.delete(b, np.s_[6 * T:7 * T], axis=2))
     assert np.array_equal(v0, v1)
+
+
+def test_row_bound_takes_only_attended_keys():
+    """The row bound's key maximum runs over the keys the row attends, not over
+    all keys (vatt-ghern section 拿掉 softmax 的序列相依: the shift is the query
+    norm times the largest key norm the row can meet).  One key of the last
+    frame is scaled 50x; rows whose frames cannot see that frame must keep a
+    bound strictly below the all-keys value, and every row's bound must equal
+    an explicit loop over the frames it attends."""
+    p = Pattern(4, 32, 1, 0)   # frame f sees frames f-1 and f only
+    q, k, _ = random_qkv(1, 2, p.seq_len, 16, seed=5)
+    kf = bf16_bits_to_f32(k).astype(np.float32)
+    kf[:, :, 3 * 32 + 7] *= 50.0   # a key of frame 3, seen by frame 3 only
+    from synth import f32_to_bf16_bits
+    k = f32_to_bf16_bits(kf)
+    scale = 0.25
+    got = NM.row_bound(q, k, p, scale)
+    qf, kw = A.widen(q), A.widen(k)
+    knorm = [[math.sqrt(math.fsum(x * x for x in kw[0, h, j])) for j in range(p.seq_len)] for h in range(2)]
+    for h in range(2):
+        all_max = max(knorm[h])
+        for i in range(p.seq_len):
+            f = i // 32
+            seen = [g for g in range(4) if f - 1 <= g <= f]
+            kmax = max(knorm[h][j] for g in seen for j in range(32 * g, 32 * g + 32))
+            qn = math.sqrt(math.fsum(x * x for x in qf[0, h, i]))
+            want = scale * qn * kmax
+            assert abs(got[0, h, i] - want) <= 1e-12 * want
+            if f < 3:
+                # the outlier lies outside this row's frames: strictly below
+                assert got[0, h, i] < 0.5 * scale * qn * all_max
+            else:
+                assert got[0, h, i] == pytest.approx(scale * qn * all_max, rel=1e-12)

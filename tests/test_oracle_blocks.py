@@ -104,3 +104,62 @@ def test_alignment_assertions_fire():
         BL.derive_blocks(Pattern(2, 40, 1, 1), 32)   # T not a multiple of 16
     with pytest.raises(ValueError):
         BL.derive_blocks(Pattern(2, 48, 1, 1), 24)   # block_q not a multiple of 16
+
+
+def granular_by_pairs(p, granule, block_q):
+    """The frame-unaware block list by plain loops over every (row, key) pair:
+    tiles of block_q rows and key blocks of `granule` keys cut from token 0;
+    a block is absent when no pair attends, full when every pair does, partial
+    otherwise; a tile's intervals are the maximal runs of present blocks of one
+    kind (full or partial), ascending."""
+    T = p.tokens_per_frame
+    N = p.num_frames * T
+
+    def sees(i, j):
+        d = j // T - i // T
+        return -p.win_before <= d <= p.win_after or (j // T) in p.global_frames
+
+    q_tiles, kv_ptr, kv_iv, kv_flag = [], [0], [], []
+    for qs in range(0, N, block_q):
+        qe = min(qs + block_q, N)
+        kinds = []
+        for ks in range(0, N, granule):
+            ke = min(ks + granule, N)
+            hit = sum(1 for i in range(qs, qe) for j in range(ks, ke) if sees(i, j))
+            kinds.append((ks, ke, "none" if hit == 0 else "full" if hit == (qe - qs) * (ke - ks) else "part"))
+        run = None
+        for ks, ke, kind in kinds + [(N, N, "none")]:
+            if run is not None and kind != run[2]:
+                kv_iv.append((run[0], run[1] - run[0]))
+                kv_flag.append(1 if run[2] == "part" else 0)
+                run = None
+            if kind != "none":
+                run = [run[0], ke, kind] if run is not None else [ks, ke, kind]
+        q_tiles.append((qs, qe - qs))
+        kv_ptr.append(len(kv_iv))
+    return q_tiles, kv_ptr, kv_iv, kv_flag
+
+
+def test_granular_derivation_brute_force():
+    """derive_blocks_granular against the per-pair enumeration on random small
+    patterns (vatt-ghern section 把 block 縮到 16; bytechap "How it works": the
+    frame-unaware layout keeps partly masked blocks and marks them).  The
+    enumeration fixes coverage (no attended pair outside the runs, no block
+    without an attended pair inside them) and the flags; maximality is checked
+    on its own: neighbouring runs of a tile leave a gap or change flag."""
+    rnd = random.Random(31)
+    for _ in range(25):
+        F = rnd.randint(1, 5)
+        T = 16 * rnd.randint(4, 8)
+        gl = tuple(sorted(set(rnd.randint(0, F - 1) for _ in range(rnd.randint(0, 2)))))
+        p = Pattern(F, T, rnd.randint(0, 2), rnd.randint(0, 2), gl)
+        granule = rnd.choice([64, 128])
+        bq = 16 * rnd.randint(1, 10)
+        qt, kp, kv, fl = granular_by_pairs(p, granule, bq)
+        got = BL.derive_blocks_granular(p, granule, bq, check_rows="all")
+        assert got["q_tiles"] == qt and got["kv_ptr"] == kp, p
+        assert got["kv_iv"] == kv and got["kv_flag"] == fl, p
+        for t in range(len(qt)):
+            runs = list(zip(kv[kp[t]:kp[t + 1]], fl[kp[t]:kp[t + 1]]))
+            for ((a0, l0), f0), ((a1, _), f1) in zip(runs, runs[1:]):
+                assert a0 + l0 < a1 or f0 != f1
