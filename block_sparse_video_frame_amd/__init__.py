@@ -183,9 +183,24 @@ class DeviceBlocks:
     kv_flag: object = None
     num_xcd: int = 8
     # The persistent launch's slot counters (attn_blocks_t.work_ctr) or None.
-    # Calls that use the same DeviceBlocks must not overlap: one stream, or
-    # ordered by events.
+    # Calls that use the same counters must not overlap; order_on() keeps
+    # them ordered across streams.
     work_ctr: object = None
+    _last_stream: object = None
+
+    def order_on(self, stream) -> None:
+        """Called before each launch that uses ``work_ctr`` on ``stream``: when
+        the previous such launch went to another stream, ``stream`` first waits
+        for everything queued on that stream so far (``wait_stream`` records an
+        event there), so two calls never hand out items from the same counters
+        at once.  On a single stream this does nothing.  Not itself
+        thread-safe: threads sharing one DeviceBlocks must serialise calls."""
+        if self.work_ctr is None:
+            return
+        last = self._last_stream
+        if last is not None and last != stream:
+            stream.wait_stream(last)
+        self._last_stream = stream
 
     def c_struct(self) -> _Blocks:
         return _Blocks(self.q_tiles.data_ptr(), self.kv_ptr.data_ptr(), self.kv_iv.data_ptr(),
@@ -402,6 +417,7 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
     cb = blocks.c_struct()
+    blocks.order_on(torch.cuda.current_stream(q.device))
     qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
     so = shift_out.data_ptr() if shift_out is not None else None
     hp = head_path.data_ptr() if head_path is not None else None

@@ -27,13 +27,19 @@
  *     been written and nothing launched; attn_last_error() gives a message
  *     (per calling thread).
  *   - Every buffer is owned by the caller.  The library allocates no memory
- *     and keeps no state between calls; it never synchronizes.  Device work is
- *     enqueued on the caller's stream and the call returns at once.  A device
- *     fault surfaces at the caller's next synchronization.
+ *     and keeps no state of its own between calls; it never synchronizes.
+ *     Device work is enqueued on the caller's stream and the call returns at
+ *     once.  A device fault surfaces at the caller's next synchronization.
+ *     The one piece of state that outlives a call is the caller-given
+ *     workspace attn_blocks_t.work_ctr (counters every call leaves zero).
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary CPU memory.
  *   - bf16 tensors are passed as const void* to raw 16-bit bf16 storage.
- *   - The functions are thread-safe (no shared mutable state).
+ *   - The library holds no global mutable state, so calls from several
+ *     threads are safe as long as they share no output buffer and no
+ *     work_ctr workspace: calls that share a workspace must be ordered (one
+ *     stream, or a stream that waits on the other's work), because each call
+ *     hands out its work through those counters and resets them at its end.
  */
 #ifndef BSVF_H
 #define BSVF_H
@@ -102,6 +108,10 @@ const char* attn_last_error(void);          /* last failure on this thread */
 
 /*
  * attn_build_blocks — host, integer only, deterministic.
+ * The frame-aligned block list (vatt-ghern "deep-heygen-avatar-iv-trillium-tpu",
+ * section 把 block 縮到 16: blocks are multiples of 16 tokens whose edges sit
+ * on frame edges, so every block is wholly attended or absent; bytechap "How
+ * it works"; cloudcurated Wall 2).
  * The block list of a pattern at query tile size block_q, canonical form:
  *   q_tiles [n_qt][2] = (first token, rows).  Frame-major; frame f is cut
  *       into T / block_q tiles of block_q rows from token f*T, then one tail
@@ -223,13 +233,21 @@ typedef struct attn_blocks_t {
                                 bound ones.  The caller zeroes it once before its
                                 first use; every call leaves it zero again.
                                 Calls that share it must not overlap (one
-                                stream, or ordered by events).  NULL: one
+                                stream, or a stream that waits for the other
+                                stream's call); overlapping calls would split
+                                each other's items and leave outputs partly
+                                unwritten, undetected.  NULL: one
                                 workgroup per item, in work_order's fixed
                                 order. */
 } attn_blocks_t;
 
 /*
- * attn_fwd — device: the block-sparse attention forward pass.
+ * attn_fwd — device: the block-sparse attention forward pass over the
+ * frame-aligned block list (vatt-ghern "deep-heygen-avatar-iv-trillium-tpu",
+ * section 把 block 縮到 16), with either the online running-max softmax or
+ * the Cauchy-Schwarz shift fixed before the key loop from precomputed norms
+ * and a per-head fallback to the running max (same page, section
+ * 拿掉 softmax 的序列相依; cloudcurated Wall 3).
  *   O[b,h,i,:] = sum_j P_ij v_j,  P_ij = exp(s_ij - m_i) / l_i over the keys j
  *   the tile of row i attends, s_ij = scale * <q_i, k_j>,
  *   LSE[b,h,i] = m_i + ln l_i  (natural log).

@@ -409,3 +409,31 @@ def test_device_blocks_workspace():
     assert blk.to_device(cpu, 1, 2, persistent=False).c_struct().work_ctr is None
     assert blk.to_device(cpu, 1, 2, schedule=False).work_ctr is None
     assert blk.to_device(cpu, 1, 2, num_xcd=3).work_ctr.numel() == 4
+
+
+def test_device_blocks_orders_calls_across_streams():
+    """Launches that share the slot counters are ordered across streams: a call
+    on a new stream first waits for the previous stream's work; a call on the
+    same stream adds nothing; a static list (no counters) never waits."""
+    blk = bs.build_blocks_for(Pattern(2, 32, 1, 1), 32)
+    cpu = __import__("torch").device("cpu")
+
+    class FakeStream:
+        def __init__(self, name, log):
+            self.name, self.log = name, log
+
+        def wait_stream(self, other):
+            self.log.append((self.name, other.name))
+
+    log = []
+    a, b = FakeStream("a", log), FakeStream("b", log)
+    d = blk.to_device(cpu, 1, 2)
+    for s in (a, a, b, b, a, b):
+        d.order_on(s)
+    assert log == [("b", "a"), ("a", "b"), ("b", "a")]
+    log.clear()
+    st = blk.to_device(cpu, 1, 2, persistent=False)
+    for s in (a, b, a):
+        st.order_on(s)
+    assert log == []
+
