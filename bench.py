@@ -134,14 +134,96 @@ def time_producer(bs, wl, q, k, dev, steps: int, warmup: int):
             "source_hash": source_hash("attn_qk_prep")}
 
 
+def time_modes(bs, wl, dev, steps: int, warmup: int, modes=(0, 1), tensors=None):
+    """attn_fwd per softmax mode on one workload, each timed by events on the
+    launch stream over `steps` calls after `warmup`; the bound modes also time
+    attn_norms, which their step includes.  Returns {mode: (fwd_ms, norms_ms)}
+    and the head paths of the last bound call."""
+    import torch
+    from synth import make_qkv
+    B, H, N, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
+    if tensors is None:
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = (up(x) for x in make_qkv(wl))
+    else:
+        q, k, v = tensors
+    blocks = bs.build_blocks_for(wl.pattern, bs.MAX_BLOCK_Q)
+    dblk = blocks.to_device(dev, B, H)
+    nm = (torch.empty(B, H, N, dtype=torch.float32, device=dev),
+          torch.empty(B, H, N // 16, dtype=torch.float32, device=dev),
+          torch.empty(B, H, 2, dtype=torch.float32, device=dev))
+    o = torch.empty(B, H, N, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
+    hp = torch.zeros(B, H, dtype=torch.int32, device=dev)
+    out, paths = {}, None
+    for mode in modes:
+        bound = mode != bs.SOFTMAX_ONLINE
+
+        def run(ev=None):
+            if bound:
+                if ev:
+                    ev[0].record()
+                bs.norms(q, k, out=nm)
+            if ev:
+                ev[1].record()
+            bs.attention(q, k, v, dblk, wl.scale, mode, norms=nm if bound else None, out=o, lse=lse,
+                         head_path=hp)
+            if ev:
+                ev[2].record()
+
+        for _ in range(warmup):
+            run()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            run(e)
+        torch.cuda.synchronize()
+        fwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        nms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if bound else 0.0
+        out[mode] = (fwd, nms)
+        if bound:
+            paths = hp.cpu().tolist()
+    return out, paths, 4.0 * D * blocks.useful_pairs * B * H
+
+
+def companions(bs, wl_main, tensors, dev, steps: int, warmup: int, others):
+    """The bound-vs-online comparison on the headline workload (same run, same
+    tensors) and on the other workloads: per workload, attn_fwd in mode 0 and
+    mode 1, attn_norms, and the ratios mode-0 time / mode-1 time for the
+    kernel alone and for the step (mode 1 with its norms pass)."""
+    import torch
+    from synth import WORKLOADS
+    res = {}
+    for name in [wl_main.name] + [n for n in others if n != wl_main.name]:
+        wl = WORKLOADS[name]
+        t, paths, flop = time_modes(bs, wl, dev, steps, warmup, tensors=tensors if name == wl_main.name else None)
+        (f0, _), (f1, n1) = t[0], t[1]
+        res[name] = {"mode0_fwd_ms": round(f0, 4), "mode1_fwd_ms": round(f1, 4), "mode1_norms_ms": round(n1, 4),
+                     "kernel_ratio": round(f0 / f1, 4), "step_ratio": round(f0 / (f1 + n1), 4),
+                     "mode1_fwd_tflops": round(flop / (f1 * 1e-3) / 1e12, 2),
+                     "mode1_fwd_frac": round(flop / (f1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "mode1_bound_heads": int(sum(sum(r) for r in paths)), "heads": wl.batch * wl.heads}
+        print(f"[bench] {name}: attn_fwd mode 0 {f0:.3f} ms, mode 1 {f1:.3f} ms (+ norms {n1:.3f}); "
+              f"kernel ratio {f0 / f1:.3f}, step ratio {f0 / (f1 + n1):.3f}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, q, k, v, target_s: float):
     """The fp64 oracle, timed on a bounded sample of query rows of the workload."""
     from oracle import attention as OA
     try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cores = os.cpu_count() or 1
+    try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        blas = host_cores
+    # the oracle is one process whose only parallel part is BLAS
+    threads = min(blas, host_cores)
     T = wl.pattern.tokens_per_frame
     F = wl.pattern.num_frames
     rng = np.random.default_rng(1)
@@ -165,6 +247,7 @@ def cpu_baseline(wl, q, k, v, target_s: float):
         useful += sum(4.0 * wl.head_dim * keys_of(int(r)) for r in rows)
         n = int(min(4096, max(64, n * max(1.0, min(4.0, (target_s - spent) / max(dt, 1e-3) / 2)))))
     return {"value": useful / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cores": int(host_cores), "blas_threads": int(blas),
             "sample": f"{rows_done} random query rows of head 0 of the {wl.name} workload, "
                       f"fp64 dense masked attention over all {wl.seq_len} keys, {spent:.1f} s"}
 
@@ -184,6 +267,9 @@ def main():
     ap.add_argument("--producer", action="store_true",
                     help="also time attn_qk_prep (QK RMS norm + rotary, norms in its epilogue) against the "
                          "same producer without norms followed by attn_norms")
+    ap.add_argument("--companions", default="1080p,sr,stress",
+                    help="after the headline, time modes 0 and 1 on the headline workload and on these "
+                         "workloads (comma list; 'none' to skip) for the bound-vs-online ratios")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (reference for the byte counters)")
     args = ap.parse_args()
@@ -305,6 +391,12 @@ def main():
     }
     if args.producer:
         res["qk_prep"] = time_producer(bs, wl, q, k, dev, args.steps, args.warmup)
+    if args.companions != "none" and args.layout == "aligned16":
+        others = [x for x in args.companions.split(",") if x]
+        comp = companions(bs, wl, (q, k, v), dev, max(5, min(args.steps, 10)), max(2, min(args.warmup, 3)),
+                          others)
+        res["bound_vs_online"] = comp[wl.name]
+        res["workloads"] = {n: c for n, c in comp.items() if n != wl.name}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, qb, kb, vb, args.cpu_seconds)

@@ -700,6 +700,9 @@ struct Tile {
 // LDS counters alone.
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+#ifndef ISSUE_LAG
+#define ISSUE_LAG 1
+#endif
 // Stages in flight ahead of the one being consumed, and LDS buffers: the
 // prefetch window, the stage being consumed, and the lagging half's previous
 // stage (see run_tile).
@@ -796,7 +799,19 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
                                          int e0, int e1, int wave, bool active) {
   using C = Cfg<D, NQB, NW>;
   using TT = Tile<D, NQB, NW, BOUND>;
-  constexpr int LOADS = 2 * C::LPW;  // vector memory ops per wave per stage
+  // Stage copies are issued by the issuing waves only: the lagging half
+  // (ISSUE_LAG), each wave taking twice the share, right after it has issued
+  // the transposing V reads of its P*V step.  The compiler orders every LDS
+  // read of that kind after all LDS-DMA copies the wave has in flight (it
+  // cannot tell the buffers apart), so a wave that issued the copies before
+  // its V reads would wait for them to land -- the full copy latency, every
+  // stage.  Issued after the reads, the copies are waited for only at the
+  // next stage's barrier, and the leading waves never wait on them.
+  constexpr int IW = ISSUE_LAG ? NW / 2 : NW;  // issuing waves
+  constexpr bool kIssuer = !ISSUE_LAG || LAG;
+  using CI = Cfg<D, NQB, IW>;
+  constexpr int LOADS = 2 * CI::LPW;  // vector memory ops per issuing wave per stage
+  const int iwave = ISSUE_LAG ? wave - NW / 2 : wave;
   static_assert((kBuffers & (kBuffers - 1)) == 0, "buffer count must be a power of two");
   const uint32_t ksn = (uint32_t)a.sk[2], vsn = (uint32_t)a.sv[2];
   const __amdgpu_buffer_rsrc_t kr = head_rsrc(kh, 2u * (ksn * (uint32_t)(a.N - 1) + D));
@@ -823,17 +838,19 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
       if (masked) T.apply_mask(sc_x, a, k0, x == ns - 1 ? nlast : BK);
     }
   };
-  DmaLanes<D, NQB, NW> dl;
-  dl.init(ksn, vsn, wave, T.lane);
+  DmaLanes<D, NQB, IW> dl;
+  if constexpr (kIssuer) dl.init(ksn, vsn, iwave, T.lane);
   auto issue = [&](int x) {
     StageDesc sd;
     int start;
-    if (kw.next(sd, start)) issue_stage_run<D, NQB, NW>(kbuf(x), kr, vr, dl, ksn, vsn, start, wave);
-    else issue_stage<D, NQB, NW>(kbuf(x), kr, vr, ksn, vsn, sd, wave, T.lane);
+    if (kw.next(sd, start)) issue_stage_run<D, NQB, IW>(kbuf(x), kr, vr, dl, ksn, vsn, start, iwave);
+    else issue_stage<D, NQB, IW>(kbuf(x), kr, vr, ksn, vsn, sd, iwave, T.lane);
   };
+  if constexpr (kIssuer) {
 #pragma unroll
-  for (int x = 0; x < kPrefetch; ++x)
-    if (x < ns) issue(x);
+    for (int x = 0; x < kPrefetch; ++x)
+      if (x < ns) issue(x);
+  }
   __builtin_amdgcn_s_waitcnt(wait_vm((kPrefetch - 1) * LOADS));  // stage 0 landed, if it was not alone
   if (ns < kPrefetch) __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
@@ -848,13 +865,26 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
     if (st + kPrefetch - 1 < ns) __builtin_amdgcn_s_waitcnt(wait_vm((kPrefetch - 2) * LOADS));
     else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (st + kPrefetch < ns) issue(st + kPrefetch);
-    if (!active) return;
+    const bool more = st + kPrefetch < ns;
+    if constexpr (!ISSUE_LAG) {
+      if (more) issue(st + kPrefetch);
+    }
+    if (!active) {
+      if constexpr (ISSUE_LAG && LAG) {
+        if (more) issue(st + kPrefetch);
+      }
+      return;
+    }
     mask_stage(cur, st);
     if constexpr (LAG) {
       if (st > 0) {
         T.pv(sm, boff(st - 1), pk);
         pin_pv<4 * C::DBLK * NQB>();
+      }
+      if constexpr (ISSUE_LAG) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) issue(st + kPrefetch);
+        __builtin_amdgcn_sched_barrier(0);
       }
       T.template softmax_and_scores<BOUND>(cur, sm, boff(st + 1), nxt, pk, alpha, a.c2);
       if constexpr (!BOUND) T.rescale(alpha);
