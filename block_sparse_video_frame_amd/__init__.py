@@ -33,7 +33,7 @@ SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE = 0, 1, 
 PATH_ONLINE, PATH_BOUND = 0, 1
 MAX_BLOCK_Q = 256
 ELIGIBLE_NATS = 60.0
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -106,6 +106,8 @@ def lib():
     L.attn_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_int32, _I64P, ctypes.c_float,
                            ctypes.POINTER(_Blocks), _VP, _VP, _VP, ctypes.c_int32, _VP, _VP]
+    L.attn_fwd_noalloc.restype = ctypes.c_int
+    L.attn_fwd_noalloc.argtypes = L.attn_fwd.argtypes
     L.attn_qk_prep.restype = ctypes.c_int
     L.attn_qk_prep.argtypes = [_VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                ctypes.c_int32, _I64P, _VP, _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP, _VP]
@@ -383,12 +385,16 @@ def qk_prep(q_in, k_in, q_gamma, k_gamma, rope_cos, rope_sin, eps: float = 1e-6,
 
 
 def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: int = SOFTMAX_BOUND,
-              norms=None, out=None, lse=None, shift_out=None, head_path=None):
+              norms=None, out=None, lse=None, shift_out=None, head_path=None, noalloc: bool = False):
     """Block-sparse attention forward (``attn_fwd``; ``attn_fwd_masked`` for
     blocks of :func:`build_blocks_granular`); returns ``(out, lse)``.
 
     ``norms``: the ``(q_norm, k_gmax, head_max)`` triple from :func:`norms`
     (computed here when the mode needs it and none is given).
+    ``noalloc``: call ``attn_fwd_noalloc`` instead, whose persistent launch
+    keeps its counters in the library (the block list needs a launch order;
+    its own counters are not used).  Pass ``out``, ``lse`` and ``norms`` to
+    allocate nothing here either.
     """
     import torch
     if q.dim() != 4:
@@ -417,11 +423,20 @@ def attention(q, k, v, blocks: DeviceBlocks, scale: float | None = None, mode: i
         lse = torch.empty(B, H, N, dtype=torch.float32, device=q.device)
     st = (ctypes.c_int64 * 12)(*(_strides(q) + _strides(k) + _strides(v) + _strides(out)))
     cb = blocks.c_struct()
-    blocks.order_on(torch.cuda.current_stream(q.device))
+    if noalloc:
+        if blocks.kv_flag is not None or blocks.work_order is None:
+            raise ValueError("noalloc needs a frame-aligned block list with a launch order")
+        cb.work_ctr = None
+    else:
+        blocks.order_on(torch.cuda.current_stream(q.device))
     qn, kg, hm = (x.data_ptr() for x in nm) if nm is not None else (None, None, None)
     so = shift_out.data_ptr() if shift_out is not None else None
     hp = head_path.data_ptr() if head_path is not None else None
-    if blocks.kv_flag is None:
+    if noalloc:
+        _check(lib().attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      so, B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb), qn, kg, hm,
+                                      mode, hp, _stream(q)))
+    elif blocks.kv_flag is None:
         _check(lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), so,
                               B, H, N, D, st, ctypes.c_float(scale), ctypes.byref(cb), qn, kg, hm, mode,
                               hp, _stream(q)))

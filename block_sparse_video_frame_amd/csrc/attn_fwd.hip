@@ -45,6 +45,8 @@
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
+#include <mutex>
+
 namespace bsvf {
 namespace {
 
@@ -1360,6 +1362,47 @@ int launch(const FwdArgs& a, int grid, hipStream_t stream) {
   return ok();
 }
 
+// Sets n counters to zero (vector stores), before a persistent launch that
+// takes its slot counters from the library's own array (attn_fwd_noalloc).
+__global__ __launch_bounds__(64) void zero_counters(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+}  // namespace
+}  // namespace bsvf
+
+// The slot counters of attn_fwd_noalloc's persistent launch: a fixed array
+// in device memory, one copy per GPU, held until the process ends.  Host
+// code never names it as an address: each device's copy is found once with
+// hipGetSymbolAddress (noalloc_counters below) and passed to the kernels.
+static __device__ __align__(256) int32_t scratch[64];
+static_assert(ATTN_NOALLOC_MAX_XCD + 1 <= 64, "scratch holds the counters of up to ATTN_NOALLOC_MAX_XCD queues");
+
+namespace bsvf {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+int noalloc_counters(int32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ATTN_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_E_UNSUPPORTED, "attn_fwd_noalloc supports device indices below 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ATTN_E_HIP, std::string("hipGetSymbolAddress of the counter array failed: ") + hipGetErrorString(e));
+    g_scratch[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return ok();
+}
+
 }  // namespace
 }  // namespace bsvf
 
@@ -1369,7 +1412,8 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
                      int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim, const int64_t* strides,
                      float scale, const attn_blocks_t* blocks, const int32_t* kv_flag,
                      const attn_pattern_t* pattern, const float* q_norm, const float* k_gmax,
-                     const float* head_max, int32_t softmax_mode, int32_t* head_path_out, hipStream_t stream) {
+                     const float* head_max, int32_t softmax_mode, int32_t* head_path_out, hipStream_t stream,
+                     bool noalloc = false) {
   const bool masked = pattern != nullptr;
   if (batch <= 0 || heads <= 0 || seq_len <= 0) return fail(ATTN_E_INVAL, "sizes must be positive");
   if (head_dim != 64 && head_dim != 128) return fail(ATTN_E_UNSUPPORTED, "head_dim must be 64 or 128");
@@ -1450,12 +1494,22 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   a.gbits[1] = (uint32_t)(gbits >> 32);
 
   if (blocks->work_ctr) {
+    if (noalloc) return fail(ATTN_E_INVAL, "attn_fwd_noalloc keeps its counters itself: blocks->work_ctr must be NULL");
     if (!blocks->work_order) return fail(ATTN_E_INVAL, "work_ctr needs a work_order");
     if (blocks->num_xcd < 1 || blocks->num_xcd > 32) return fail(ATTN_E_INVAL, "num_xcd must be in [1, 32]");
     if (blocks->n_work % blocks->num_xcd) return fail(ATTN_E_INVAL, "n_work must be a multiple of num_xcd");
   }
-  a.n_xcd = blocks->work_ctr ? blocks->num_xcd : 1;
-  a.work_ctr = blocks->work_ctr;
+  if (noalloc) {
+    if (!blocks->work_order) return fail(ATTN_E_INVAL, "attn_fwd_noalloc needs a work_order (from attn_build_schedule)");
+    if (blocks->num_xcd < 1) return fail(ATTN_E_INVAL, "num_xcd must be at least 1");
+    if (blocks->num_xcd > ATTN_NOALLOC_MAX_XCD)
+      return fail(ATTN_E_SIZE, "attn_fwd_noalloc holds counters for at most ATTN_NOALLOC_MAX_XCD (32) queues");
+    if (blocks->n_work % blocks->num_xcd) return fail(ATTN_E_INVAL, "n_work must be a multiple of num_xcd");
+  }
+  int32_t* ctr = blocks->work_ctr;
+  if (noalloc && (st = noalloc_counters(&ctr))) return st;
+  a.n_xcd = ctr ? blocks->num_xcd : 1;
+  a.work_ctr = ctr;
   const int grid = blocks->work_order ? blocks->n_work : (int)items;
   const int bq_bound = 32 * BOUND_NQB * BOUND_NW, bq_online = 32 * ONLINE_NQB * ONLINE_NW;
   if (blocks->block_q > (softmax_mode == ATTN_SOFTMAX_BOUND_FORCED ? bq_bound
@@ -1466,7 +1520,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   // mode its kernel holds the online path only.  Without one, each path has
   // a launch of one workgroup per item.
   int cus = 0;
-  if (blocks->work_ctr) {
+  if (ctr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
@@ -1475,6 +1529,12 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (cus > 0) {
     const int pgrid = std::min(blocks->n_work, cus);
     const bool both = softmax_mode != ATTN_SOFTMAX_ONLINE;
+    if (noalloc) {
+      // the shared array keeps the last call's contents: start from zero
+      hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, stream, ctr, blocks->num_xcd + 1);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+    }
     if (masked)
       st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream)
                            : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream);
@@ -1512,6 +1572,16 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         hipStream_t stream) {
   return fwd_entry(q, k, v, o, lse, shift_out, batch, heads, seq_len, head_dim, strides, scale, blocks,
                    nullptr, nullptr, q_norm, k_gmax, head_max, softmax_mode, head_path_out, stream);
+}
+
+extern "C" int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+                                int32_t head_dim, const int64_t* strides, float scale,
+                                const attn_blocks_t* blocks, const float* q_norm, const float* k_gmax,
+                                const float* head_max, int32_t softmax_mode, int32_t* head_path_out,
+                                hipStream_t stream) {
+  return fwd_entry(q, k, v, o, lse, shift_out, batch, heads, seq_len, head_dim, strides, scale, blocks,
+                   nullptr, nullptr, q_norm, k_gmax, head_max, softmax_mode, head_path_out, stream, true);
 }
 
 extern "C" int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BSVF_ABI_VERSION 2
+#define BSVF_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -284,6 +284,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              const attn_blocks_t* blocks, const float* q_norm,
              const float* k_gmax, const float* head_max, int32_t softmax_mode,
              int32_t* head_path_out, hipStream_t stream);
+
+/* Largest num_xcd attn_fwd_noalloc accepts (its counter array holds
+ * ATTN_NOALLOC_MAX_XCD + 1 int32). */
+#define ATTN_NOALLOC_MAX_XCD 32
+
+/*
+ * attn_fwd_noalloc — device; attn_fwd for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as attn_fwd, with these differences:
+ *   - blocks->work_ctr must be NULL: the persistent launch's slot counters
+ *     live in a fixed array of the library (ATTN_NOALLOC_MAX_XCD + 1 int32 in
+ *     device memory, one copy per GPU, held until the process ends), which
+ *     each call clears with a one-workgroup kernel on `stream` before its
+ *     launch;
+ *   - blocks->work_order is required (the persistent launch's queues), and
+ *     blocks->num_xcd must be in [1, ATTN_NOALLOC_MAX_XCD]: ATTN_E_SIZE above
+ *     it, ATTN_E_INVAL for NULL work_order, a non-NULL work_ctr, num_xcd < 1 or
+ *     n_work not a multiple of num_xcd;
+ *   - the call allocates nothing (no hipMalloc, hipFree or allocating library
+ *     routine).  Its first call on a device looks the array up there
+ *     (hipGetSymbolAddress); ATTN_E_HIP if that fails, ATTN_E_UNSUPPORTED for
+ *     a device index above 63.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams, or several threads) race and may leave outputs partly
+ * unwritten.  Order them (one stream, or events).
+ */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,
+                     int32_t head_dim, const int64_t* strides, float scale,
+                     const attn_blocks_t* blocks, const float* q_norm,
+                     const float* k_gmax, const float* head_max, int32_t softmax_mode,
+                     int32_t* head_path_out, hipStream_t stream);
 
 /*
  * attn_fwd_masked — device; attn_fwd over the frame-unaware layout of

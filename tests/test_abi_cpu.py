@@ -208,7 +208,7 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="validation-only test fo
 FAKE = 0x10000  # 16-byte aligned, never dereferenced
 
 
-def fwd_call(**over):
+def fwd_call(entry="attn_fwd", **over):
     L = bs.lib()
     args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, shift=None, B=1, H=2, N=192, D=64,
                 strides=[192 * 64 * 2, 192 * 64, 64] * 4, scale=0.125, blocks="ok",
@@ -220,7 +220,7 @@ def fwd_call(**over):
         for k, v in args["blocks"].items():
             setattr(cb, k, v)
     bp = ctypes.byref(cb) if args["blocks"] is not None else None
-    return L.attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["shift"],
+    return getattr(L, entry)(args["q"], args["k"], args["v"], args["o"], args["lse"], args["shift"],
                       args["B"], args["H"], args["N"], args["D"], st, ctypes.c_float(args["scale"]), bp,
                       args["qn"], args["kg"], args["hm"], args["mode"], args["hp"], None)
 
@@ -253,6 +253,22 @@ def fwd_call(**over):
 ])
 def test_fwd_validation(over, status):
     assert fwd_call(**over) == status
+    assert bs.lib().attn_last_error().startswith(bs.lib().attn_status_str(status))
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(), 1),                                                               # no work_order
+    (dict(blocks={"work_order": FAKE, "n_work": 16, "num_xcd": 8, "work_ctr": FAKE}), 1),  # its own counters given
+    (dict(blocks={"work_order": FAKE, "n_work": 66, "num_xcd": 33}), 4),       # beyond the counter array
+    (dict(blocks={"work_order": FAKE, "n_work": 16, "num_xcd": 0}), 1),
+    (dict(blocks={"work_order": FAKE, "n_work": 12, "num_xcd": 8}), 1),        # not whole queues
+    (dict(q=None, blocks={"work_order": FAKE, "n_work": 16, "num_xcd": 8}), 1),
+])
+def test_fwd_noalloc_validation(over, status):
+    """attn_fwd_noalloc rejects what it cannot run before any HIP call: no launch
+    order, a caller workspace, more queues than its counter array holds."""
+    assert fwd_call("attn_fwd_noalloc", **over) == status
     assert bs.lib().attn_last_error().startswith(bs.lib().attn_status_str(status))
 
 
