@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "PATH_ONLINE", "PATH_BOUND",
-    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "AttnError", "lib", "library_path", "abi_version",
+    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "PRESCALE_NATS", "AttnError", "lib", "library_path", "abi_version",
     "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "qk_prep",
     "attention",
 ]
@@ -33,6 +33,7 @@ SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE = 0, 1, 
 PATH_ONLINE, PATH_BOUND = 0, 1
 MAX_BLOCK_Q = 256
 ELIGIBLE_NATS = 60.0
+PRESCALE_NATS = 40.0
 ABI_VERSION = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -64,11 +64,19 @@ constexpr int BK = 64;  // keys per LDS stage
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// The bound path keeps Q pre-multiplied by scale*log2(e) and rounded to bf16
-// (each element off by at most 2^-9 relative), so its scores can exceed
-// scale*log2(e)*|q|*|k| by that much; the margin covers it with room for the
-// fp32 dot-product and norm rounding (below D * 2^-24 for D <= 128).
+// The fixed shift is the bound times this margin, which keeps it above every
+// score the kernel computes: the fp32 dot products and the fp32 norms each
+// carry rounding error below D * 2^-24 relative for D <= 128, far inside 2^-8.
 constexpr float kBoundMargin = 1.0f + 1.0f / 256.0f;
+// Bound rows come in two kinds.  Where the slack bound is at most
+// ATTN_PRESCALE_NATS, the bound loop keeps Q multiplied by scale*log2(e) and
+// rounded to bf16 once, and starts the score accumulator at -m, so the MFMA
+// yields the exponent directly (no FMA per score).  That rounding moves a
+// score by up to 2^-9 of |q||k| (scale*|q||k| is at most half the slack
+// bound), which near the eligibility limit would cost most of the error
+// budget.  Rows with a looser bound keep Q exact and take the exponent with
+// one FMA per score: they run on the online loop with its running max
+// switched off (a fixed shift).
 // s_getreg operand for the XCC id hardware register (id 20, bits 31:0)
 constexpr int kHwRegXccId = (31 << 11) | 20;
 
@@ -319,6 +327,7 @@ struct Tile {
   bf16x8 qreg[NQB][C::KSTEPS];
   f32x16 oacc[NQB][C::DBLK];
   float m2[NQB];    // row shift in log2 units (bound: fixed; online: running max)
+  bool fixed;       // online loop with a fixed shift (the bound with exact Q): no max, no rescale
   float lsum[NQB];   // this lane half's share of the row sum
   float lsum2[NQB];  // a second running sum, fed where a chunk holds two pairs (D = 64)
   int n, hh, lane;
@@ -331,8 +340,9 @@ struct Tile {
     return *(const volatile lds_bf16x8*)(sm + (((boff | lof.kl) ^ (32u * st)) + 32u * RS * kb));
   }
 
-  // Score accumulators start at acc0[qb]: the bound path starts at -m (its Q
-  // already carries scale*log2(e)), so the MFMA yields the exponent directly.
+  // Score accumulators start at acc0[qb]: the bound loop starts at -m (its Q
+  // already carries scale*log2(e)), so the MFMA yields the exponent directly;
+  // the online loop (also running fixed shifts) at 0.
   __device__ __forceinline__ float acc0(int qb) const { return BOUNDQ ? -m2[qb] : 0.0f; }
 
   // S^T = K * Q^T for the 64 keys of a stage: lane (n, hh) gets keys
@@ -366,7 +376,7 @@ struct Tile {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       alpha[qb] = 1.0f;
-      if constexpr (!BOUND) {
+      if (!BOUND && !fixed) {
         // Missing keys hold copies of a real key of this row, so they cannot
         // raise the max above a real score.
         float mx = s[0][qb][0];
@@ -433,7 +443,7 @@ struct Tile {
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       alpha[qb] = 1.0f;
-      if constexpr (!BOUND) {
+      if (!BOUND && !fixed) {
         float mx = cur[0][qb][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -476,6 +486,20 @@ struct Tile {
     // holds two pairs), with no per-stage partial sums to start and fold.
     float pe[NM][NQB][EPM];        // chunk i's probabilities (fp32)
     uint32_t pp[NM][NQB][EPM / 2];  // chunk i's packed bf16 pairs
+    // The exponent of each score, s * scale * log2(e) - m, is taken one chunk
+    // ahead of its exp (xe), so the exp never waits on the FMA before it.
+    constexpr bool kFma = !BOUND;
+    float xe[NM][NQB][EPM];
+    auto arg = [&](int i) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int e = 0; e < EPM; ++e) {
+          const int el = i * EPM + e, kb = el >> 4, r = el & 15;
+          xe[i][qb][e] = kFma ? fmaf(cur[kb][qb][r], c2, nm[qb]) : cur[kb][qb][r];
+        }
+    };
+    if constexpr (kFma) arg(0);
 #pragma unroll
     for (int i = 0; i < NM + 2; ++i) {
       if (i < NM) {
@@ -492,16 +516,25 @@ struct Tile {
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
           nxt[kbn(i)][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qreg[qb][stn(i)], nxt[kbn(i)][qb], 0, 0, 0);
+        if constexpr (!kFma) arg(i);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
           for (int e = 0; e < EPM; ++e) {
-            const int el = i * EPM + e, kb = el >> 4, r = el & 15;
-            pe[i][qb][e] = __builtin_amdgcn_exp2f(BOUND ? cur[kb][qb][r] : fmaf(cur[kb][qb][r], c2, nm[qb]));
+            pe[i][qb][e] = __builtin_amdgcn_exp2f(xe[i][qb][e]);
             // keep this slice here: without a use at this point the
             // compiler sinks the whole softmax below the MFMAs
             asm volatile("" : "+v"(pe[i][qb][e]));
           }
+        if constexpr (kFma) {
+          if (i + 1 < NM) {
+            arg(i + 1);
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+              for (int e = 0; e < EPM; ++e) asm volatile("" : "+v"(xe[i + 1][qb][e]));
+          }
+        }
       }
       if (i >= 1 && i <= NM) {
         const int c = i - 1;
@@ -574,6 +607,7 @@ struct Tile {
   // Online path: apply the pending rescale to the accumulator, skipped when
   // no row of the wave raised its max.
   __device__ __forceinline__ void rescale(const float (&alpha)[NQB]) {
+    if (fixed) return;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb)
       if (__any(alpha[qb] != 1.0f)) {
@@ -644,7 +678,7 @@ struct Tile {
   template <bool BOUND, bool TAIL>
   __device__ __forceinline__ void softmax_half(const Half& s, HalfProbs& pk, float& alpha, int nvalid, float c2,
                                                int kb) {
-    alpha = BOUND ? 1.0f : raise_max(s, c2);
+    alpha = (BOUND || fixed) ? 1.0f : raise_max(s, c2);
     const float nm = m2[0] == -INFINITY ? 0.0f : -m2[0];
     float p[16];
 #pragma unroll
@@ -670,7 +704,7 @@ struct Tile {
   }
 
   __device__ __forceinline__ void rescale_half(float alpha) {
-    if (__any(alpha != 1.0f)) {
+    if (!fixed && __any(alpha != 1.0f)) {
 #pragma unroll
       for (int db = 0; db < C::DBLK; ++db) oacc[0][db] *= alpha;
     }
@@ -1068,20 +1102,27 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
   e1 = max(e0, min(e1, a.nnz));
 
   // Softmax path: uniform per workgroup; per head (modes 1, 2) or per tile
-  // (mode 3, which needs the tile's largest query and key norms first).
+  // (mode 3, which needs the tile's largest query and key norms first).  A
+  // slack bound within ATTN_PRESCALE_NATS takes the bound loop (prescaled
+  // Q); up to ATTN_ELIGIBLE_NATS the online loop with the bound as a fixed
+  // shift (exact Q); beyond it the running max.  Forced mode: bound loop.
+  enum { kOnline = 0, kExact = 1, kPre = 2 };
+  auto classify = [](float slack) {
+    return slack <= ATTN_PRESCALE_NATS ? kPre : slack <= ATTN_ELIGIBLE_NATS ? kExact : kOnline;
+  };
   const bool per_tile = a.mode == ATTN_SOFTMAX_BOUND_TILE;
-  bool bound = false;
+  int path = kOnline;
   if (a.mode == ATTN_SOFTMAX_BOUND_FORCED) {
-    bound = true;
+    path = kPre;
   } else if (a.mode == ATTN_SOFTMAX_BOUND) {
     const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
-    bound = 2.0f * a.scale * mq * mk <= ATTN_ELIGIBLE_NATS;
+    path = classify(2.0f * a.scale * mq * mk);
   }
-  if (!per_tile && bound != BOUND) return false;
+  if (!per_tile && (path == kPre) != BOUND) return false;
 
   // Tile-wide max key norm over every attended 16-key granule.
   float km = 0.0f;
-  if (BOUND || per_tile) {
+  if (BOUND || per_tile || path == kExact) {
     float* red = reinterpret_cast<float*>(smem + C::STAGE);
     const cf32* kg = k_gmax + (int64_t)bh * (a.N / 16);
     for (int e = e0; e < e1; ++e) {
@@ -1103,16 +1144,22 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
     qm = red[NW];
 #pragma unroll
     for (int i = 1; i < NW; ++i) { km = fmaxf(km, red[i]); qm = fmaxf(qm, red[NW + i]); }
-    if (per_tile) bound = 2.0f * a.scale * qm * km <= ATTN_ELIGIBLE_NATS;
+    // the same in every lane: keep them in scalar registers
+    km = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, km)));
+    qm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, qm)));
+    if (per_tile) path = classify(2.0f * a.scale * qm * km);
     // `red` lies in a stage buffer that the first copies below overwrite:
     // every wave has to have read it first
     __syncthreads();
   }
-  if (bound != BOUND) return false;
-  if (tile == 0 && tid == 0 && a.head_path_out) a.head_path_out[bh] = bound ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
-  const float kfac = BOUND ? a.scale * km * kBoundMargin : 0.0f;
+  if ((path == kPre) != BOUND) return false;
+  const bool fixed = !BOUND && path == kExact;
+  if (tile == 0 && tid == 0 && a.head_path_out)
+    a.head_path_out[bh] = path != kOnline ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
+  const float kfac = (BOUND || fixed) ? a.scale * km * kBoundMargin : 0.0f;
 
   Tile<D, NQB, NW, BOUND> T;
+  T.fixed = __builtin_amdgcn_readfirstlane(fixed ? 1 : 0) != 0;
   T.n = lane & 31;
   T.hh = lane >> 5;
   T.lane = lane;
@@ -1144,7 +1191,7 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
       }
       T.qreg[qb][st] = valid ? x : z;
     }
-    if constexpr (BOUND) {
+    if (BOUND || T.fixed) {
       const float qn = q_norm[(int64_t)bh * a.N + qs + (valid ? r : 0)];
       T.m2[qb] = valid ? qn * kfac * kLog2e : 0.0f;
     } else {

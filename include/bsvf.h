@@ -70,7 +70,8 @@ enum {
 enum {
   ATTN_SOFTMAX_ONLINE = 0,       /* running max with rescaling, every head */
   ATTN_SOFTMAX_BOUND = 1,        /* Cauchy-Schwarz shift on eligible heads,
-                                    online fallback on the rest (the method) */
+                                    online fallback on the rest (the method);
+                                    see ATTN_PRESCALE_NATS */
   ATTN_SOFTMAX_BOUND_FORCED = 2, /* bound on every head (diagnostic only: may
                                     underflow to l = 0 on loose heads) */
   ATTN_SOFTMAX_BOUND_TILE = 3    /* the eligibility test per query tile instead
@@ -91,6 +92,13 @@ enum { ATTN_PATH_ONLINE = 0, ATTN_PATH_BOUND = 1 };
  * This caps the gap between the fixed shift and the true row max, so the
  * largest term exp(s - m) stays far above the float32/bf16 normal range. */
 #define ATTN_ELIGIBLE_NATS 60.0f
+
+/* Eligible heads (or tiles, mode 3) whose slack bound is at most
+ * ATTN_PRESCALE_NATS run with Q multiplied by scale*log2(e) and rounded to
+ * bf16 once (no multiply per score); the others keep Q exact and scale each
+ * score (the rounding moves a score by up to 2^-9 of scale*|q||k|, which
+ * matters only for large logits).  Both use the same fixed shift. */
+#define ATTN_PRESCALE_NATS 40.0f
 
 /* Frame-window pattern (host struct). */
 typedef struct attn_pattern_t {
@@ -268,8 +276,10 @@ typedef struct attn_blocks_t {
  *       not ATTN_SOFTMAX_ONLINE, ignored (may be NULL) otherwise.
  *   softmax_mode: ATTN_SOFTMAX_*.  The bound shift is
  *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-8);
- *       the factor keeps it above every score the kernel computes (the bound
- *       path multiplies Q by scale*log2(e) and rounds it to bf16 once).
+ *       the factor keeps it above every score the kernel computes (fp32 dot
+ *       products and norms).  Heads (tiles, mode 3) whose slack bound is at
+ *       most ATTN_PRESCALE_NATS, and every head in mode 2, use Q multiplied
+ *       by scale*log2(e) and rounded to bf16 once; the rest use Q as given.
  *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head
  *       (for ATTN_SOFTMAX_BOUND_TILE: the path of the head's first tile).
  * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,

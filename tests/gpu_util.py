@@ -3,6 +3,9 @@ sampled rows, and the tolerance check against the fp64 oracle.
 """
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 
 # Float tolerances of the parity bar: O max |err| <= 1e-2, mean |err| <= 1e-3,
@@ -78,3 +81,12 @@ def errors(o, lse, o_ref, lse_ref):
 
 def within(e) -> bool:
     return e["max_abs"] <= TOL_MAX_ABS and e["mean_abs"] <= TOL_MEAN_ABS and e["lse_rel"] <= TOL_LSE_REL
+
+
+def record(test: str, case: str, mode: int, e: dict) -> None:
+    """Appends one parity measurement (errors against the oracle) as a JSON
+    line to the file named by BSVF_PARITY_LOG, when that is set."""
+    path = os.environ.get("BSVF_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": test, "case": case, "mode": int(mode), **e}) + "\n")

@@ -15,12 +15,12 @@ import pytest
 
 from oracle import attention as OA
 from oracle import norms as ON
-from synth import WORKLOADS, Pattern, make_qkv, random_qkv
+from synth import WORKLOADS, Pattern, bf16_bits_to_f32, f32_to_bf16_bits, make_qkv, random_qkv
 
 pytestmark = pytest.mark.gpu
 
 import block_sparse_video_frame_amd as bs
-from gpu_util import errors, run_gpu, sample_rows, within
+from gpu_util import errors, record, run_gpu, sample_rows, within
 
 _INPUTS = {}
 _ORACLE = {}
@@ -86,6 +86,7 @@ def test_small_all_rows(case, mode):
     res = run_gpu(q, k, v, p, scale, mode, block_q=bq)
     O, L = OA.attention(q, k, v, p, scale)
     e = errors(res["o"], res["lse"], O, L)
+    record("small_all_rows", str(case), mode, e)
     assert within(e), e
     # every query row was written
     assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
@@ -101,8 +102,57 @@ def test_workload_sampled_rows(name, mode):
     O, L = oracle_rows(name, rows)
     e = errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L)
     print(name, mode, e)
+    record("workload_sampled_rows", name, mode, e)
     assert within(e), e
     assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
+
+
+def near_limit_qkv(B, H, N, D, seed, target, heavy):
+    """Seeded N(0,1) Q, K, V whose heads are scaled so that the head-wide slack
+    bound 2 * scale * max|q| * max|k| is about `target` nats, just inside the
+    eligibility limit: the bound path then runs with its largest logits.
+    With `heavy`, 1% of the key rows are doubled first, so a few keys set
+    max|k| and most rows keep a slack far above their row maximum."""
+    q, k, v = random_qkv(B, H, N, D, seed=seed)
+    qf = bf16_bits_to_f32(q).copy()
+    kf = bf16_bits_to_f32(k).copy()
+    if heavy:
+        sel = np.random.default_rng(seed + 1000).random((B, H, N)) < 0.01
+        kf[sel] *= np.float32(2.0)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    qn = np.sqrt((qf.astype(np.float64) ** 2).sum(-1)).max(-1)
+    kn = np.sqrt((kf.astype(np.float64) ** 2).sum(-1)).max(-1)
+    c = np.sqrt(target / (2.0 * scale * qn * kn)).astype(np.float32)[..., None, None]
+    return f32_to_bf16_bits(qf * c), f32_to_bf16_bits(kf * c), v
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("heavy", [False, True])
+@pytest.mark.parametrize("mode", [1, 3, 0])
+def test_near_limit_eligible_heads(D, heavy, mode):
+    """Heads whose slack bound sits at 55-59 nats, just inside the 60-nat
+    limit, take the bound path in modes 1 and 3 and still meet the plain
+    absolute band on every row: the largest logits the bound path accepts,
+    where the rounding of Q * scale * log2(e) to bf16 weighs most."""
+    p = Pattern(6, 256, 1, 1, (0,))
+    B, H = 1, 4
+    q, k, v = near_limit_qkv(B, H, p.seq_len, D, seed=40 + D + heavy, target=57.0, heavy=heavy)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    sl = ON.slack_bound(ON.head_max(ON.row_norms(q), ON.row_norms(k)), scale)
+    assert ((sl >= 55.0) & (sl <= 59.0)).all(), sl
+    res = run_gpu(q, k, v, p, scale, mode)
+    O, L = OA.attention(q, k, v, p, scale)
+    e = errors(res["o"], res["lse"], O, L)
+    print(D, heavy, mode, e)
+    record("near_limit", f"D{D}{'_heavy' if heavy else ''}", mode, e)
+    assert within(e), e
+    assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
+    if mode == 1:
+        assert (res["head_path"] == bs.PATH_BOUND).all()
+    if mode in (1, 3):
+        # every row ran on the bound: its shift is the bound times (1 + 2^-8)
+        bd = ON.row_bound(q, k, p, scale)
+        assert np.allclose(res["shift"], bd * (1 + 2.0 ** -8), rtol=1e-5)
 
 
 def test_stress_forced_bound_underflows():
@@ -341,6 +391,8 @@ def test_hot_frame_workload(mode):
     s = np.maximum(1.0, np.abs(O))
     e = errors(res["o"][:, :, rows] / s, res["lse"][:, :, rows], O / s, L)
     print(name, mode, e)
+    record("hot_frame_scaled", name, mode, e)
+    record("hot_frame_plain", name, mode, errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L))
     assert within(e), e
     assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
     head = ON.slack_bound(ON.head_max(ON.row_norms(q), ON.row_norms(k)), wl.scale)
