@@ -197,13 +197,19 @@ def companions(bs, wl_main, tensors, dev, steps: int, warmup: int, others):
     res = {}
     for name in [wl_main.name] + [n for n in others if n != wl_main.name]:
         wl = WORKLOADS[name]
-        t, paths, flop = time_modes(bs, wl, dev, steps, warmup, tensors=tensors if name == wl_main.name else None)
+        main = name == wl_main.name
+        t, paths, flop = time_modes(bs, wl, dev, steps, warmup, modes=(0, 1, 4) if main else (0, 1),
+                                    tensors=tensors if main else None)
         (f0, _), (f1, n1) = t[0], t[1]
         res[name] = {"mode0_fwd_ms": round(f0, 4), "mode1_fwd_ms": round(f1, 4), "mode1_norms_ms": round(n1, 4),
                      "kernel_ratio": round(f0 / f1, 4), "step_ratio": round(f0 / (f1 + n1), 4),
                      "mode1_fwd_tflops": round(flop / (f1 * 1e-3) / 1e12, 2),
                      "mode1_fwd_frac": round(flop / (f1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "mode1_bound_heads": int(sum(sum(r) for r in paths)), "heads": wl.batch * wl.heads}
+        if 4 in t:
+            # the bound with Q never rounded (every eligible head scales each score)
+            res[name]["mode4_fwd_ms"] = round(t[4][0], 4)
+            res[name]["mode4_kernel_ratio"] = round(f0 / t[4][0], 4)
         print(f"[bench] {name}: attn_fwd mode 0 {f0:.3f} ms, mode 1 {f1:.3f} ms (+ norms {n1:.3f}); "
               f"kernel ratio {f0 / f1:.3f}, step ratio {f0 / (f1 + n1):.3f}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()

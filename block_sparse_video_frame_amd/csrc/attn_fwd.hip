@@ -1114,9 +1114,10 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
   int path = kOnline;
   if (a.mode == ATTN_SOFTMAX_BOUND_FORCED) {
     path = kPre;
-  } else if (a.mode == ATTN_SOFTMAX_BOUND) {
+  } else if (a.mode == ATTN_SOFTMAX_BOUND || a.mode == ATTN_SOFTMAX_BOUND_EXACT) {
     const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
     path = classify(2.0f * a.scale * mq * mk);
+    if (a.mode == ATTN_SOFTMAX_BOUND_EXACT && path == kPre) path = kExact;  // never rounds Q
   }
   if (!per_tile && (path == kPre) != BOUND) return false;
 
@@ -1467,7 +1468,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (seq_len % 16) return fail(ATTN_E_ALIGN, "seq_len must be a multiple of 16");
   if (!strides) return fail(ATTN_E_INVAL, "strides is NULL");
   if (!(scale > 0.0f) || !(scale < 3.0e38f)) return fail(ATTN_E_INVAL, "scale must be positive and finite");
-  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_TILE)
+  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_EXACT)
     return fail(ATTN_E_INVAL, "bad softmax_mode");
   int st;
   if ((st = check_tensor("q", q, strides + 0, batch, heads, seq_len, head_dim))) return st;
@@ -1575,7 +1576,8 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   }
   if (cus > 0) {
     const int pgrid = std::min(blocks->n_work, cus);
-    const bool both = softmax_mode != ATTN_SOFTMAX_ONLINE;
+    // the bound loop is needed unless every item runs on the online loop
+    const bool both = softmax_mode != ATTN_SOFTMAX_ONLINE && softmax_mode != ATTN_SOFTMAX_BOUND_EXACT;
     if (noalloc) {
       // the shared array keeps the last call's contents: start from zero
       hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, stream, ctr, blocks->num_xcd + 1);
@@ -1590,7 +1592,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
                            : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, stream);
     return st ? st : ok();
   }
-  if (softmax_mode != ATTN_SOFTMAX_ONLINE) {
+  if (softmax_mode != ATTN_SOFTMAX_ONLINE && softmax_mode != ATTN_SOFTMAX_BOUND_EXACT) {
     if (masked)
       st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
                            : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream);

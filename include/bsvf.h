@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BSVF_ABI_VERSION 3
+#define BSVF_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -74,11 +74,15 @@ enum {
                                     see ATTN_PRESCALE_NATS */
   ATTN_SOFTMAX_BOUND_FORCED = 2, /* bound on every head (diagnostic only: may
                                     underflow to l = 0 on loose heads) */
-  ATTN_SOFTMAX_BOUND_TILE = 3    /* the eligibility test per query tile instead
+  ATTN_SOFTMAX_BOUND_TILE = 3,   /* the eligibility test per query tile instead
                                     of per head: a tile takes the bound when
                                     2 * scale * max|q| over its rows * max|k|
                                     over its attended keys <= ATTN_ELIGIBLE_NATS,
                                     else the running max */
+  ATTN_SOFTMAX_BOUND_EXACT = 4   /* as ATTN_SOFTMAX_BOUND, but no head uses the
+                                    prescaled Q of ATTN_PRESCALE_NATS: every
+                                    bound head scales each score instead
+                                    (slower, Q never rounded) */
 };
 
 /* Values written to head_path_out. */
@@ -278,8 +282,9 @@ typedef struct attn_blocks_t {
  *       m_i = scale * |q_i| * max{k_gmax over the tile's intervals} * (1 + 2^-8);
  *       the factor keeps it above every score the kernel computes (fp32 dot
  *       products and norms).  Heads (tiles, mode 3) whose slack bound is at
- *       most ATTN_PRESCALE_NATS, and every head in mode 2, use Q multiplied
- *       by scale*log2(e) and rounded to bf16 once; the rest use Q as given.
+ *       most ATTN_PRESCALE_NATS (except in mode 4), and every head in mode 2,
+ *       use Q multiplied by scale*log2(e) and rounded to bf16 once; the rest
+ *       use Q as given.
  *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head
  *       (for ATTN_SOFTMAX_BOUND_TILE: the path of the head's first tile).
  * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,

@@ -78,7 +78,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 def test_small_all_rows(case, mode):
     p, B, H, D, bq = SMALL[case]
     q, k, v = random_qkv(B, H, p.seq_len, D, seed=100 + case)
@@ -93,7 +93,7 @@ def test_small_all_rows(case, mode):
 
 
 @pytest.mark.parametrize("name", [n for n in WORKLOADS if n != "hotframe"])   # hotframe: its own test
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 4])
 def test_workload_sampled_rows(name, mode):
     wl = WORKLOADS[name]
     q, k, v = inputs(name)
@@ -128,7 +128,7 @@ def near_limit_qkv(B, H, N, D, seed, target, heavy):
 
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("heavy", [False, True])
-@pytest.mark.parametrize("mode", [1, 3, 0])
+@pytest.mark.parametrize("mode", [1, 3, 4, 0])
 def test_near_limit_eligible_heads(D, heavy, mode):
     """Heads whose slack bound sits at 55-59 nats, just inside the 60-nat
     limit, take the bound path in modes 1 and 3 and still meet the plain
@@ -147,9 +147,9 @@ def test_near_limit_eligible_heads(D, heavy, mode):
     record("near_limit", f"D{D}{'_heavy' if heavy else ''}", mode, e)
     assert within(e), e
     assert np.isfinite(res["o"]).all() and np.isfinite(res["lse"]).all()
-    if mode == 1:
+    if mode in (1, 4):
         assert (res["head_path"] == bs.PATH_BOUND).all()
-    if mode in (1, 3):
+    if mode in (1, 3, 4):
         # every row ran on the bound: its shift is the bound times (1 + 2^-8)
         bd = ON.row_bound(q, k, p, scale)
         assert np.allclose(res["shift"], bd * (1 + 2.0 ** -8), rtol=1e-5)
@@ -176,17 +176,18 @@ def test_head_path_matches_oracle_eligibility(name):
     sl = ON.slack_bound(hm, wl.scale)
     assert (np.abs(sl - ON.ELIGIBLE_NATS) > 1e-3 * ON.ELIGIBLE_NATS).all()
     want = ON.eligible(hm, wl.scale).astype(np.int32)
-    for mode, expect in [(0, np.zeros_like(want)), (1, want), (2, np.ones_like(want))]:
+    for mode, expect in [(0, np.zeros_like(want)), (1, want), (2, np.ones_like(want)), (4, want)]:
         res = run_gpu(q, k, v, wl.pattern, wl.scale, mode)
         assert (res["head_path"] == expect).all(), (mode, res["head_path"], expect)
 
 
 @pytest.mark.parametrize("name", ["tiny", "720p", "sr"])
-def test_bound_never_below_row_max(name):
+@pytest.mark.parametrize("mode", [1, 4])
+def test_bound_never_below_row_max(name, mode):
     wl = WORKLOADS[name]
     q, k, v = inputs(name)
     rows = rows_for(name)
-    res = run_gpu(q, k, v, wl.pattern, wl.scale, bs.SOFTMAX_BOUND)
+    res = run_gpu(q, k, v, wl.pattern, wl.scale, mode)
     mx = OA.scores_max(q, k, wl.pattern, wl.scale, rows=rows)
     shift = res["shift"][:, :, rows]
     assert (shift >= mx).all()
@@ -196,7 +197,7 @@ def test_bound_never_below_row_max(name):
     assert (np.abs(shift - bd * (1 + 2.0 ** -8)) <= 1e-5 * np.maximum(bd, 1.0)).all()
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", [0, 1, 4])
 def test_bitwise_deterministic(mode):
     wl = WORKLOADS["720p"]
     q, k, v = inputs("720p")
