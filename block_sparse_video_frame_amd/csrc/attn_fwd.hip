@@ -131,7 +131,8 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
 }
 
 // p0 + p1 + acc for a packed bf16 pair (one v_dot2 with (1, 1)): the row sum
-// adds exactly the rounded probabilities the P*V product uses.
+// adds exactly the rounded probabilities the P*V product uses.  A v_dot2
+// cannot issue while a matrix instruction is running; plain fp32 adds can.
 __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
@@ -329,7 +330,13 @@ struct Tile {
   float m2[NQB];    // row shift in log2 units (bound: fixed; online: running max)
   bool fixed;       // online loop with a fixed shift (the bound with exact Q): no max, no rescale
   float lsum[NQB];   // this lane half's share of the row sum
-  float lsum2[NQB];  // a second running sum, fed where a chunk holds two pairs (D = 64)
+  float lsum2[NQB];  // a second running sum (the second pair of a chunk at D = 64,
+                     // the odd probabilities at D = 128)
+  // Row sums.  At D = 128 a stage has twice the matrix work per probability,
+  // enough to hide two fp32 adds per pair under the MFMAs, and the sums add
+  // the fp32 probabilities.  At D = 64 the vector unit is the tighter one and
+  // a v_dot2 per pair sums them as rounded to bf16 for the P*V product.
+  static constexpr bool kSumF32 = D == 128;
   int n, hh, lane;
   int fq[NQB];  // frame of this lane's query row (frame-unaware layout only)
   LaneOffsets<D> lof;
@@ -416,11 +423,19 @@ struct Tile {
       for (int kb = 0; kb < 2; ++kb) {
         pk[qb][kb][0] = to_bf16x8(p[kb]);
         pk[qb][kb][1] = to_bf16x8(p[kb] + 8);
+        if constexpr (kSumF32) {
 #pragma unroll
-        for (int kst = 0; kst < 2; ++kst) {
-          const u32x4 w = __builtin_bit_cast(u32x4, pk[qb][kb][kst]);
-          t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
-          t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+          for (int r = 0; r < 16; r += 2) {
+            t0 += p[kb][r];
+            t1 += p[kb][r + 1];
+          }
+        } else {
+#pragma unroll
+          for (int kst = 0; kst < 2; ++kst) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pk[qb][kb][kst]);
+            t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
+            t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+          }
         }
       }
       lsum[qb] += t0 + t1;
@@ -457,7 +472,7 @@ struct Tile {
         alpha[qb] = __builtin_amdgcn_exp2f(m2[qb] - msafe);
         m2[qb] = mnew;
         lsum[qb] *= alpha[qb];
-        if constexpr (EPM > 2) lsum2[qb] *= alpha[qb];
+        if constexpr (EPM > 2 || kSumF32) lsum2[qb] *= alpha[qb];
       }
       nm[qb] = m2[qb] == -INFINITY ? 0.0f : -m2[qb];
     }
@@ -484,6 +499,8 @@ struct Tile {
     // wave's matrix and vector work then interleave without stalls.  Pairs
     // go straight into the running row sums (the second one where a chunk
     // holds two pairs), with no per-stage partial sums to start and fold.
+    // The fp32 sums of D = 128 are added in chunk i+1, beside the conversion
+    // (kept to chunk i+2, the probabilities would need more registers).
     float pe[NM][NQB][EPM];        // chunk i's probabilities (fp32)
     uint32_t pp[NM][NQB][EPM / 2];  // chunk i's packed bf16 pairs
     // The exponent of each score, s * scale * log2(e) - m, is taken one chunk
@@ -548,6 +565,10 @@ struct Tile {
             asm volatile("" : "+v"(w));
             pp[c][qb][e >> 1] = w;
             pw[qb][kb][r >> 1] = w;
+            if constexpr (kSumF32) {
+              lsum[qb] += pe[c][qb][e];
+              lsum2[qb] += pe[c][qb][e + 1];
+            }
           }
       }
       if (i >= 2) {
@@ -556,8 +577,13 @@ struct Tile {
         for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
           for (int e = 0; e < EPM; e += 2) {
-            if ((e >> 1) & 1) lsum2[qb] = add_pair(pp[c][qb][e >> 1], lsum2[qb]);
-            else lsum[qb] = add_pair(pp[c][qb][e >> 1], lsum[qb]);
+            if constexpr (kSumF32) {
+              // summed in chunk i+1
+            } else if ((e >> 1) & 1) {
+              lsum2[qb] = add_pair(pp[c][qb][e >> 1], lsum2[qb]);
+            } else {
+              lsum[qb] = add_pair(pp[c][qb][e >> 1], lsum[qb]);
+            }
           }
           asm volatile("" : "+v"(lsum[qb]), "+v"(lsum2[qb]));
         }
@@ -694,11 +720,19 @@ struct Tile {
     pk[0] = to_bf16x8(p);
     pk[1] = to_bf16x8(p + 8);
     float t0 = 0.0f, t1 = 0.0f;
+    if constexpr (kSumF32) {
 #pragma unroll
-    for (int kst = 0; kst < 2; ++kst) {
-      const u32x4 w = __builtin_bit_cast(u32x4, pk[kst]);
-      t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
-      t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+      for (int r = 0; r < 16; r += 2) {
+        t0 += p[r];
+        t1 += p[r + 1];
+      }
+    } else {
+#pragma unroll
+      for (int kst = 0; kst < 2; ++kst) {
+        const u32x4 w = __builtin_bit_cast(u32x4, pk[kst]);
+        t0 = add_pair(w[0], t0); t1 = add_pair(w[1], t1);
+        t0 = add_pair(w[2], t0); t1 = add_pair(w[3], t1);
+      }
     }
     lsum[0] += t0 + t1;
   }
