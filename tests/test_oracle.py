@@ -280,3 +280,75 @@ def test_row_bound_takes_only_attended_keys():
                 assert got[0, h, i] < 0.5 * scale * qn * all_max
             else:
                 assert got[0, h, i] == pytest.approx(scale * qn * all_max, rel=1e-12)
+
+
+def checked_inputs():
+    """Four 32-token frames, D 16, every key close to +e0 (|k| about 1).  Query
+    rows by frame: 0 aligned with e0, |q| 40 (certificate about 80 nats, every
+    row's largest term near 1); 1 the same but one row anti-aligned (its terms
+    all near e^-80); 2 aligned with |q| 10 (certificate about 20); 3 aligned
+    with |q| 200 (certificate about 400)."""
+    from synth import f32_to_bf16_bits
+    p = Pattern(4, 32, 1, 0)
+    rng = np.random.default_rng(11)
+    D, N = 16, p.seq_len
+    e0 = np.zeros(D, np.float32); e0[0] = 1.0
+    k = (e0 + np.float32(0.1) * rng.standard_normal((1, 1, N, D), dtype=np.float32)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = (e0 + np.float32(0.05) * rng.standard_normal((1, 1, N, D), dtype=np.float32)).astype(np.float32)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    q[0, 0, 0:64] *= 40.0
+    q[0, 0, 32 + 5] = -40.0 * e0
+    q[0, 0, 64:96] *= 10.0
+    q[0, 0, 96:128] *= 200.0
+    v = rng.standard_normal((1, 1, N, D), dtype=np.float32)
+    return p, f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def test_checked_tile_paths_pins():
+    """The checked per-tile test against explicit loops: per row the bound shift
+    (the query norm times the largest attended key norm), l by math.fsum of
+    exp(s - m), and the tile's path from its certificate and the smallest ln l
+    (kept iff l >= 2^-100 in every row).  The four frames give one tile of each
+    kind: checked and kept, checked and rejected by one row, certified, and
+    beyond the check limit."""
+    p, q, k, v = checked_inputs()
+    scale = 1.0
+    tiles = [(0, 32), (32, 32), (64, 32), (96, 32)]
+    paths, min_ln_l = NM.checked_tile_paths(q, k, v, p, scale, tiles)
+    qf, kf = A.widen(q)[0, 0], A.widen(k)[0, 0]
+    norm = lambda x: math.sqrt(math.fsum(float(t) * float(t) for t in x))
+    want_paths = []
+    for t, (qs, nr) in enumerate(tiles):
+        keys = [j for j in range(p.seq_len) if -1 <= j // 32 - t <= 0]
+        kmax = max(norm(kf[j]) for j in keys)
+        cert = 2 * scale * max(norm(qf[i]) for i in range(qs, qs + nr)) * kmax
+        if cert <= NM.ELIGIBLE_NATS:
+            want_paths.append(1)
+            assert math.isnan(min_ln_l[0, 0, t])
+            continue
+        if cert > NM.CHECK_NATS:
+            want_paths.append(0)
+            assert math.isnan(min_ln_l[0, 0, t])
+            continue
+        lows = []
+        for i in range(qs, qs + nr):
+            m = scale * norm(qf[i]) * kmax
+            s = [scale * math.fsum(float(a) * float(b) for a, b in zip(qf[i], kf[j])) for j in keys]
+            lows.append(math.log(math.fsum(math.exp(x - m) for x in s)))
+        assert abs(min(lows) - min_ln_l[0, 0, t]) <= 1e-9 * abs(min(lows)) + 1e-12
+        want_paths.append(2 if min(lows) >= -100.0 * math.log(2.0) else 0)
+    assert list(paths[0, 0]) == want_paths == [2, 0, 1, 0]
+    assert min_ln_l[0, 0, 0] > -5.0 and min_ln_l[0, 0, 1] < -70.0
+
+
+def test_checked_tile_paths_reduce_to_the_tile_test():
+    """Where every tile's certificate is within the eligibility limit the
+    checked test evaluates nothing and agrees with the per-tile test."""
+    p = Pattern(5, 48, 1, 1, (0,))
+    q, k, v = small(p)
+    tiles = [(f * 48, 48) for f in range(5)]
+    cert = NM.tile_slack_bound(q, k, p, 0.125, tiles)
+    assert (cert <= NM.ELIGIBLE_NATS).all()
+    paths, min_ln_l = NM.checked_tile_paths(q, k, v, p, 0.125, tiles)
+    assert (paths == 1).all() and np.isnan(min_ln_l).all()
