@@ -138,7 +138,7 @@ def time_modes(bs, wl, dev, steps: int, warmup: int, modes=(0, 1), tensors=None)
     """attn_fwd per softmax mode on one workload, each timed by events on the
     launch stream over `steps` calls after `warmup`; the bound modes also time
     attn_norms, which their step includes.  Returns {mode: (fwd_ms, norms_ms)}
-    and the head paths of the last bound call."""
+    and the head paths of the mode-1 call."""
     import torch
     from synth import make_qkv
     B, H, N, D = wl.batch, wl.heads, wl.seq_len, wl.head_dim
@@ -182,34 +182,44 @@ def time_modes(bs, wl, dev, steps: int, warmup: int, modes=(0, 1), tensors=None)
         fwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
         nms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if bound else 0.0
         out[mode] = (fwd, nms)
-        if bound:
+        if mode == bs.SOFTMAX_BOUND:
             paths = hp.cpu().tolist()
     return out, paths, 4.0 * D * blocks.useful_pairs * B * H
+
+
+# Modes timed on a companion workload besides 0 and 1: the per-tile and the
+# checked per-tile test where heads fail the per-head test on part of their
+# tiles (hotframe) or on every certificate while their rows stay close to the
+# bound (spread).
+EXTRA_MODES = {"hotframe": (3, 5), "spread": (3, 5)}
 
 
 def companions(bs, wl_main, tensors, dev, steps: int, warmup: int, others):
     """The bound-vs-online comparison on the headline workload (same run, same
     tensors) and on the other workloads: per workload, attn_fwd in mode 0 and
     mode 1, attn_norms, and the ratios mode-0 time / mode-1 time for the
-    kernel alone and for the step (mode 1 with its norms pass)."""
+    kernel alone and for the step (mode 1 with its norms pass); modes 4 (the
+    headline workload) and 3 and 5 (EXTRA_MODES) with their kernel ratios
+    against mode 0."""
     import torch
     from synth import WORKLOADS
     res = {}
     for name in [wl_main.name] + [n for n in others if n != wl_main.name]:
         wl = WORKLOADS[name]
         main = name == wl_main.name
-        t, paths, flop = time_modes(bs, wl, dev, steps, warmup, modes=(0, 1, 4) if main else (0, 1),
-                                    tensors=tensors if main else None)
+        modes = (0, 1, 4) if main else (0, 1) + EXTRA_MODES.get(name, ())
+        t, paths, flop = time_modes(bs, wl, dev, steps, warmup, modes=modes, tensors=tensors if main else None)
         (f0, _), (f1, n1) = t[0], t[1]
         res[name] = {"mode0_fwd_ms": round(f0, 4), "mode1_fwd_ms": round(f1, 4), "mode1_norms_ms": round(n1, 4),
                      "kernel_ratio": round(f0 / f1, 4), "step_ratio": round(f0 / (f1 + n1), 4),
                      "mode1_fwd_tflops": round(flop / (f1 * 1e-3) / 1e12, 2),
                      "mode1_fwd_frac": round(flop / (f1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "mode1_bound_heads": int(sum(sum(r) for r in paths)), "heads": wl.batch * wl.heads}
-        if 4 in t:
-            # the bound with Q never rounded (every eligible head scales each score)
-            res[name]["mode4_fwd_ms"] = round(t[4][0], 4)
-            res[name]["mode4_kernel_ratio"] = round(f0 / t[4][0], 4)
+        for m in (3, 4, 5):
+            # 4: the bound with Q never rounded; 3: the per-tile test; 5: the checked per-tile test
+            if m in t:
+                res[name][f"mode{m}_fwd_ms"] = round(t[m][0], 4)
+                res[name][f"mode{m}_kernel_ratio"] = round(f0 / t[m][0], 4)
         print(f"[bench] {name}: attn_fwd mode 0 {f0:.3f} ms, mode 1 {f1:.3f} ms (+ norms {n1:.3f}); "
               f"kernel ratio {f0 / f1:.3f}, step ratio {f0 / (f1 + n1):.3f}", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
@@ -273,7 +283,7 @@ def main():
     ap.add_argument("--producer", action="store_true",
                     help="also time attn_qk_prep (QK RMS norm + rotary, norms in its epilogue) against the "
                          "same producer without norms followed by attn_norms")
-    ap.add_argument("--companions", default="1080p,sr,stress",
+    ap.add_argument("--companions", default="1080p,sr,stress,hotframe,spread",
                     help="after the headline, time modes 0 and 1 on the headline workload and on these "
                          "workloads (comma list; 'none' to skip) for the bound-vs-online ratios")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -23,18 +23,22 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = [
-    "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "SOFTMAX_BOUND_EXACT", "PATH_ONLINE", "PATH_BOUND",
-    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "PRESCALE_NATS", "AttnError", "lib", "library_path", "abi_version",
+    "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "SOFTMAX_BOUND_EXACT",
+    "SOFTMAX_BOUND_CHECKED", "PATH_ONLINE", "PATH_BOUND",
+    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "PRESCALE_NATS", "CHECK_NATS", "CHECK_LOG2_L", "AttnError", "lib", "library_path", "abi_version",
     "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "qk_prep",
     "attention",
 ]
 
 SOFTMAX_ONLINE, SOFTMAX_BOUND, SOFTMAX_BOUND_FORCED, SOFTMAX_BOUND_TILE, SOFTMAX_BOUND_EXACT = 0, 1, 2, 3, 4
+SOFTMAX_BOUND_CHECKED = 5
 PATH_ONLINE, PATH_BOUND = 0, 1
 MAX_BLOCK_Q = 256
 ELIGIBLE_NATS = 60.0
 PRESCALE_NATS = 40.0
-ABI_VERSION = 4
+CHECK_NATS = 256.0
+CHECK_LOG2_L = -100.0
+ABI_VERSION = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

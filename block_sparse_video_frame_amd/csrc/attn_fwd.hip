@@ -68,6 +68,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 // score the kernel computes: the fp32 dot products and the fp32 norms each
 // carry rounding error below D * 2^-24 relative for D <= 128, far inside 2^-8.
 constexpr float kBoundMargin = 1.0f + 1.0f / 256.0f;
+// Smallest row sum a checked tile keeps (2^ATTN_CHECK_LOG2_L).
+constexpr float kCheckMinL = 0x1p-100f;
+static_assert(ATTN_CHECK_LOG2_L == -100.0f, "kCheckMinL is 2^ATTN_CHECK_LOG2_L");
 // Bound rows come in two kinds.  Where the slack bound is at most
 // ATTN_PRESCALE_NATS, the bound loop keeps Q multiplied by scale*log2(e) and
 // rounded to bf16 once, and starts the score accumulator at -m, so the MFMA
@@ -136,6 +139,23 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
 __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
+// Workgroup-wide OR of one flag per wave, through the first NW words of the
+// stage array; every wave calls it.  The first barrier puts every wave past
+// its last use of the stage array (no stage copy is in flight by then), the
+// last keeps later copies off the words until every wave has read them.
+template <int NW>
+__device__ __forceinline__ bool group_any(bool flag, u16* smem, int wave, int lane) {
+  int* word = reinterpret_cast<int*>(smem);
+  __syncthreads();
+  if (lane == 0) word[wave] = flag ? 1 : 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any |= word[w];
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(any) != 0;
 }
 
 __device__ __forceinline__ bool interval_ok(int ks, int kl, int N) {
@@ -1107,15 +1127,21 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const ci32* kv_iv, u1
   }
 }
 
+// What run_item did with an item.
+enum ItemResult { kDeclined = 0, kDone = 1, kRetry = 2 };
+
 // One work item w (a query tile of one (batch, head)) on the softmax path
-// BOUND, in the stage array `smem`.  Returns false, having written nothing,
-// when the item takes the other path; true when it is done (or is no valid
-// item).  All waves of the workgroup call it and return together, except
-// that waves with no rows may return before the epilogue.
-template <int D, int NQB, int NW, bool BOUND, bool MASK>
-__device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, const ci32* kv_ptr,
-                                         const ci32* kv_iv, const cf32* k_gmax, const cf32* head_max,
-                                         u16* smem, int w) {
+// BOUND, in the stage array `smem`.  Returns kDeclined, having written
+// nothing, when the item takes the other path; kRetry, having written
+// nothing, when it is a checked tile (mode 5) whose check failed -- the
+// caller runs it again with `force_online`; kDone when it is done (or is no
+// valid item).  All waves of the workgroup call it and return together,
+// except that waves with no rows may return before the epilogue.  Only
+// kernels built with CHECK (launched for mode 5) hold the check.
+template <int D, int NQB, int NW, bool BOUND, bool MASK, bool CHECK>
+__device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, const ci32* kv_ptr,
+                                        const ci32* kv_iv, const cf32* k_gmax, const cf32* head_max,
+                                        u16* smem, int w, bool force_online = false) {
   const cf32* q_norm = (const cf32*)a.q_norm;
   using C = Cfg<D, NQB, NW>;
   // The thread index is made opaque, so that the per-lane setup derived from
@@ -1126,25 +1152,33 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
   const int lane = tid & 63, wave = tid >> 6;
 
   const int total = a.n_qt * a.H * a.B;
-  if (w < 0 || w >= total) return true;
+  if (w < 0 || w >= total) return kDone;
   const int tile = w % a.n_qt, bh = w / a.n_qt;
   const int b = bh / a.H, h = bh % a.H;
   const int qs = q_tiles[2 * tile], nr = q_tiles[2 * tile + 1];
-  if (qs < 0 || nr <= 0 || nr > C::BQ || nr > a.block_q || qs > a.N - nr) return true;
+  if (qs < 0 || nr <= 0 || nr > C::BQ || nr > a.block_q || qs > a.N - nr) return kDone;
   int e0 = kv_ptr[tile], e1 = kv_ptr[tile + 1];
   e0 = max(0, min(e0, a.nnz));
   e1 = max(e0, min(e1, a.nnz));
 
-  // Softmax path: uniform per workgroup; per head (modes 1, 2) or per tile
-  // (mode 3, which needs the tile's largest query and key norms first).  A
-  // slack bound within ATTN_PRESCALE_NATS takes the bound loop (prescaled
-  // Q); up to ATTN_ELIGIBLE_NATS the online loop with the bound as a fixed
-  // shift (exact Q); beyond it the running max.  Forced mode: bound loop.
-  enum { kOnline = 0, kExact = 1, kPre = 2 };
-  auto classify = [](float slack) {
-    return slack <= ATTN_PRESCALE_NATS ? kPre : slack <= ATTN_ELIGIBLE_NATS ? kExact : kOnline;
+  // Softmax path: uniform per workgroup; per head (modes 1, 2, 4) or per
+  // tile (modes 3 and 5, which need the tile's largest query and key norms
+  // first).  A slack bound within ATTN_PRESCALE_NATS takes the bound loop
+  // (prescaled Q; not in mode 4, which never rounds Q); up to
+  // ATTN_ELIGIBLE_NATS the online loop with the bound as a fixed shift
+  // (exact Q); in mode 5, up to ATTN_CHECK_NATS the same, checked after the
+  // fact (kCheck); beyond it the running max.  Forced mode: bound loop.  A
+  // checked tile that failed runs again on the running max.
+  enum { kOnline = 0, kExact = 1, kPre = 2, kCheck = 3 };
+  // (Only kernels built with CHECK run mode 5.)
+  const bool checked = CHECK && a.mode == ATTN_SOFTMAX_BOUND_CHECKED && !force_online;
+  auto classify = [checked](float slack) {
+    return slack <= ATTN_PRESCALE_NATS ? kPre
+           : slack <= ATTN_ELIGIBLE_NATS ? kExact
+           : checked && slack <= ATTN_CHECK_NATS ? kCheck
+                                                 : kOnline;
   };
-  const bool per_tile = a.mode == ATTN_SOFTMAX_BOUND_TILE;
+  const bool per_tile = a.mode == ATTN_SOFTMAX_BOUND_TILE || a.mode == ATTN_SOFTMAX_BOUND_CHECKED;
   int path = kOnline;
   if (a.mode == ATTN_SOFTMAX_BOUND_FORCED) {
     path = kPre;
@@ -1153,7 +1187,7 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
     path = classify(2.0f * a.scale * mq * mk);
     if (a.mode == ATTN_SOFTMAX_BOUND_EXACT && path == kPre) path = kExact;  // never rounds Q
   }
-  if (!per_tile && (path == kPre) != BOUND) return false;
+  if (!per_tile && (path == kPre) != BOUND) return kDeclined;
 
   // Tile-wide max key norm over every attended 16-key granule.
   float km = 0.0f;
@@ -1187,8 +1221,11 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
     // every wave has to have read it first
     __syncthreads();
   }
-  if ((path == kPre) != BOUND) return false;
-  const bool fixed = !BOUND && path == kExact;
+  if (force_online) path = kOnline;
+  if ((path == kPre) != BOUND) return kDeclined;
+  const bool fixed = !BOUND && (path == kExact || path == kCheck);
+  // (a checked tile whose check fails runs again at once, on the running
+  // max, and overwrites this)
   if (tile == 0 && tid == 0 && a.head_path_out)
     a.head_path_out[bh] = path != kOnline ? ATTN_PATH_BOUND : ATTN_PATH_ONLINE;
   const float kfac = (BOUND || fixed) ? a.scale * km * kBoundMargin : 0.0f;
@@ -1253,12 +1290,32 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
   }
   if (thin) {
     run_thin<D, NQB, NW, BOUND>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
-    if (wv & 3) return true;  // merged into the first wave of the row group
   } else if (wv >= NW / 2) {
     run_tile<D, NQB, NW, BOUND, true, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
   } else {
     run_tile<D, NQB, NW, BOUND, false, MASK>(a, kv_iv, smem, T, kh, vh, e0, e1, wv, active);
   }
+  if constexpr (CHECK && !BOUND) {
+    // Mode 5 checks every tile that ran with a fixed shift (kExact or
+    // kCheck; a kExact tile always passes, its certificate keeps l above
+    // e^-ATTN_ELIGIBLE_NATS).  Both conditions are re-read rather than kept
+    // in a register across the walk.
+    if (T.fixed && a.mode == ATTN_SOFTMAX_BOUND_CHECKED) {
+      // Every row's full l (both lane halves; after a thin walk, held by the
+      // first wave of each row group) against 2^ATTN_CHECK_LOG2_L.
+      bool low = false;
+      if (active && (!thin || (wv & 3) == 0)) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          const float lh = T.lsum[qb] + T.lsum2[qb];
+          const float lt = lh + __shfl_xor(lh, 32);
+          low |= row0 + qb * 32 + T.n < nr && !(lt >= kCheckMinL);
+        }
+      }
+      if (group_any<NW>(__any(low), smem, wv, lane)) return kRetry;
+    }
+  }
+  if (thin && (wv & 3)) return kDone;  // merged into the first wave of the row group
 
   // Epilogue: O = O_acc / l (bf16, nearest even), LSE = m + ln l.
   u16* oh = a.o + b * a.so[0] + h * a.so[1];
@@ -1287,14 +1344,14 @@ __device__ __forceinline__ bool run_item(const FwdArgs& a, const ci32* q_tiles, 
       if (a.shift_out) a.shift_out[ri] = T.m2[qb] * kLn2;
     }
   }
-  return true;
+  return kDone;
 }
 
 // Static launch: workgroup i takes item work_order[i] (or i) on the path
 // BOUND.  Both paths are launched over the same work; a workgroup whose item
 // takes the other path exits at once, so each item is computed by exactly one
 // of them and each path gets a register allocation of its own.
-template <int D, int NQB, int NW, bool BOUND, bool MASK>
+template <int D, int NQB, int NW, bool BOUND, bool MASK, bool CHECK>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* __restrict__ q_tiles,
                                                       const int32_t* __restrict__ kv_ptr,
                                                       const int32_t* __restrict__ kv_iv,
@@ -1308,8 +1365,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(FwdArgs a, const int32_t* 
     if (w >= a.n_work) return;
     w = work_order[w];
   }
-  run_item<D, NQB, NW, BOUND, MASK>(a, (const ci32*)q_tiles, (const ci32*)kv_ptr, (const ci32*)kv_iv,
-                                    (const cf32*)k_gmax, (const cf32*)head_max, smem, w);
+  // a checked tile whose check failed runs again, on the running max
+  for (bool force = false;; force = true) {
+    const int r = run_item<D, NQB, NW, BOUND, MASK, CHECK>(a, (const ci32*)q_tiles, (const ci32*)kv_ptr,
+                                                           (const ci32*)kv_iv, (const cf32*)k_gmax,
+                                                           (const cf32*)head_max, smem, w, force);
+    if (!CHECK || r != kRetry) break;
+  }
 }
 
 // The kernel-argument segment (constant address space: scalar loads that no
@@ -1347,19 +1409,28 @@ __device__ __forceinline__ void item_args(FwdArgs& ia) {
 // of their own.  Without BOTH the kernel holds the online path alone (the
 // online mode): sharing a kernel with the bound path costs the online loop
 // about 2%.  The outputs do not depend on which workgroup computes an item.
-template <int D, int NQB, int NW, bool MASK, bool BOTH>
+template <int D, int NQB, int NW, bool MASK, bool BOTH, bool CHECK>
 __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   (void)a;  // read through the argument-segment pointer below
   using C = Cfg<D, NQB, NW>;
-  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE];
+  // The stage buffers, then 16 bytes that hold the item index: no stage copy
+  // reaches them, so a workgroup can read its item again without keeping it
+  // in a register.  (One LDS array: a separate LDS variable would cost the
+  // operand reads their overlap with the stage copies, see tile_max.)
+  __shared__ __attribute__((aligned(16))) u16 smem[kBuffers * C::STAGE + 8];
+  // [0]: the item index; [1] (CHECK): 1 while the item is to run again.
+  int32_t* const item_word = reinterpret_cast<int32_t*>(smem + kBuffers * C::STAGE);
   uint32_t empty = 0;  // thread 0: the queues found exhausted
-  // The item goes to every wave through the first word of the stage array
-  // (a separate LDS variable would cost the operand reads their overlap with
-  // the stage copies: see tile_max).
-  int32_t* const word = reinterpret_cast<int32_t*>(smem);
+  if constexpr (CHECK) {
+    if (threadIdx.x == 0) item_word[1] = 0;  // (read after the loop's first barrier)
+  }
   for (;;) {
-    __syncthreads();  // every wave is done with the previous item's LDS
-    if (threadIdx.x == 0) {
+    __syncthreads();  // every wave is done with the previous item and has read its index
+    // A checked tile whose check failed (run_item returned kRetry, in every
+    // wave) runs again, on the running max: its index stays, and the flag
+    // that says so is kept in LDS rather than in a register across the walk.
+    const bool again = CHECK && __builtin_amdgcn_readfirstlane(item_word[1]) != 0;
+    if (!again && threadIdx.x == 0) {
       // The queue layout and pointers are read here, through a pointer to
       // the kernel arguments the compiler cannot see through, rather than
       // held in scalar registers across the item (the walk needs them all).
@@ -1380,11 +1451,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
         if (cand < 0) empty |= 1u << x;
         else w = cand;
       }
-      word[0] = w;
+      item_word[0] = w;
     }
     __syncthreads();
-    const int w = __builtin_amdgcn_readfirstlane(word[0]);
-    __syncthreads();  // read by every wave before the item's copies reuse it
+    const int w = __builtin_amdgcn_readfirstlane(item_word[0]);
     if (w < 0) break;
     // Each path reads the item's arguments afresh through the opaque
     // pointer, so none is held in a scalar register from one item, or one
@@ -1392,18 +1462,26 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
     // used: see run_item)
     bool done = false;
     if constexpr (BOTH) {
-      FwdArgs ia;
-      item_args(ia);
-      done = run_item<D, NQB, NW, true, MASK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr,
-                                              (const ci32*)ia.kv_iv, (const cf32*)ia.k_gmax,
-                                              (const cf32*)ia.head_max, smem, w);
+      if (!again) {
+        FwdArgs ia;
+        item_args(ia);
+        done = run_item<D, NQB, NW, true, MASK, CHECK>(ia, (const ci32*)ia.q_tiles, (const ci32*)ia.kv_ptr,
+                                                       (const ci32*)ia.kv_iv, (const cf32*)ia.k_gmax,
+                                                       (const cf32*)ia.head_max, smem, w) != kDeclined;
+      }
     }
     if (!done) {
       FwdArgs ib;
       item_args(ib);
-      run_item<D, NQB, NW, false, MASK>(ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr,
-                                        (const ci32*)ib.kv_iv, (const cf32*)ib.k_gmax,
-                                        (const cf32*)ib.head_max, smem, w);
+      const bool force = CHECK && __builtin_amdgcn_readfirstlane(item_word[1]) != 0;
+      const int r = run_item<D, NQB, NW, false, MASK, CHECK>(ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr,
+                                                             (const ci32*)ib.kv_iv, (const cf32*)ib.k_gmax,
+                                                             (const cf32*)ib.head_max, smem, w, force);
+      if constexpr (CHECK) {
+        // (both cases walked the tile, past barriers that follow every
+        // wave's reads of the flag)
+        if (threadIdx.x == 0 && (r == kRetry || force)) item_word[1] = r == kRetry ? 1 : 0;
+      }
     }
   }
   // Leaving: work_ctr[n_xcd] counts the workgroups that are done.  The last
@@ -1427,17 +1505,36 @@ static_assert(ONLINE_NQB == BOUND_NQB && ONLINE_NW == BOUND_NW,
               "the persistent kernel runs both paths on one tile shape");
 
 template <int D, int NQB, int NW, bool MASK>
-int launch_persistent(const FwdArgs& a, int grid, bool both, hipStream_t stream) {
-  if (both) hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
-  else hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
+int launch_persistent(const FwdArgs& a, int grid, bool both, bool check, hipStream_t stream) {
+  if constexpr (!MASK) {  // (the frame-unaware layout does not take mode 5)
+    if (check) {
+      hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true, true>), dim3(grid), dim3(64 * NW), 0, stream, a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+      return ok();
+    }
+  }
+  if (both)
+    hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, false, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return ok();
 }
 
 template <int D, int NQB, int NW, bool BOUND, bool MASK>
-int launch(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND, MASK>), dim3(grid), dim3(64 * NW), 0, stream, a,
+int launch(const FwdArgs& a, int grid, bool check, hipStream_t stream) {
+  if constexpr (!BOUND && !MASK) {  // (the frame-unaware layout does not take mode 5)
+    if (check) {
+      hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND, MASK, true>), dim3(grid), dim3(64 * NW), 0, stream, a,
+                         a.q_tiles, a.kv_ptr, a.kv_iv, a.work_order, a.k_gmax, a.head_max);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
+      return ok();
+    }
+  }
+  hipLaunchKernelGGL((fwd_kernel<D, NQB, NW, BOUND, MASK, false>), dim3(grid), dim3(64 * NW), 0, stream, a,
                      a.q_tiles, a.kv_ptr, a.kv_iv, a.work_order, a.k_gmax, a.head_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
@@ -1502,8 +1599,10 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   if (seq_len % 16) return fail(ATTN_E_ALIGN, "seq_len must be a multiple of 16");
   if (!strides) return fail(ATTN_E_INVAL, "strides is NULL");
   if (!(scale > 0.0f) || !(scale < 3.0e38f)) return fail(ATTN_E_INVAL, "scale must be positive and finite");
-  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_EXACT)
+  if (softmax_mode < ATTN_SOFTMAX_ONLINE || softmax_mode > ATTN_SOFTMAX_BOUND_CHECKED)
     return fail(ATTN_E_INVAL, "bad softmax_mode");
+  if (masked && softmax_mode == ATTN_SOFTMAX_BOUND_CHECKED)
+    return fail(ATTN_E_UNSUPPORTED, "the frame-unaware layout takes softmax modes 0 to 4");
   int st;
   if ((st = check_tensor("q", q, strides + 0, batch, heads, seq_len, head_dim))) return st;
   if ((st = check_tensor("k", k, strides + 3, batch, heads, seq_len, head_dim))) return st;
@@ -1567,6 +1666,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   a.k_gmax = k_gmax;
   a.head_max = head_max;
   a.mode = softmax_mode;
+  const bool check = softmax_mode == ATTN_SOFTMAX_BOUND_CHECKED;
   a.head_path_out = head_path_out;
   a.kv_flag = kv_flag;
   a.frame_T = masked ? pattern->tokens_per_frame : 0;
@@ -1598,9 +1698,9 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
                          : softmax_mode == ATTN_SOFTMAX_ONLINE ? bq_online : min(bq_bound, bq_online)))
     return fail(ATTN_E_UNSUPPORTED, "block_q exceeds the kernels' query tile of 256 rows");
   // With a work_ctr, one persistent launch runs every item on its path (one
-  // workgroup per CU; a workgroup takes most of a CU's LDS); in the online
-  // mode its kernel holds the online path only.  Without one, each path has
-  // a launch of one workgroup per item.
+  // workgroup per CU; a workgroup takes most of a CU's LDS); in the modes
+  // without the prescaled Q (0 and 4) its kernel holds the online loop only.
+  // Without one, each path has a launch of one workgroup per item.
   int cus = 0;
   if (ctr) {
     int dev = 0;
@@ -1612,6 +1712,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
     const int pgrid = std::min(blocks->n_work, cus);
     // the bound loop is needed unless every item runs on the online loop
     const bool both = softmax_mode != ATTN_SOFTMAX_ONLINE && softmax_mode != ATTN_SOFTMAX_BOUND_EXACT;
+    // mode 5 has kernels of its own: only they hold the check and the retry
     if (noalloc) {
       // the shared array keeps the last call's contents: start from zero
       hipLaunchKernelGGL(zero_counters, dim3(1), dim3(64), 0, stream, ctr, blocks->num_xcd + 1);
@@ -1619,29 +1720,29 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
       if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
     }
     if (masked)
-      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream)
-                           : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, stream);
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, check, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, true>(a, pgrid, both, check, stream);
     else
-      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, stream)
-                           : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, stream);
+      st = head_dim == 128 ? launch_persistent<128, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, check, stream)
+                           : launch_persistent<64, BOUND_NQB, BOUND_NW, false>(a, pgrid, both, check, stream);
     return st ? st : ok();
   }
   if (softmax_mode != ATTN_SOFTMAX_ONLINE && softmax_mode != ATTN_SOFTMAX_BOUND_EXACT) {
     if (masked)
-      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream)
-                           : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, stream);
+      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, true>(a, grid, check, stream)
+                           : launch<64, BOUND_NQB, BOUND_NW, true, true>(a, grid, check, stream);
     else
-      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, false>(a, grid, stream)
-                           : launch<64, BOUND_NQB, BOUND_NW, true, false>(a, grid, stream);
+      st = head_dim == 128 ? launch<128, BOUND_NQB, BOUND_NW, true, false>(a, grid, check, stream)
+                           : launch<64, BOUND_NQB, BOUND_NW, true, false>(a, grid, check, stream);
     if (st) return st;
   }
   if (softmax_mode != ATTN_SOFTMAX_BOUND_FORCED) {
     if (masked)
-      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, stream)
-                           : launch<64, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, stream);
+      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, check, stream)
+                           : launch<64, ONLINE_NQB, ONLINE_NW, false, true>(a, grid, check, stream);
     else
-      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, stream)
-                           : launch<64, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, stream);
+      st = head_dim == 128 ? launch<128, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, check, stream)
+                           : launch<64, ONLINE_NQB, ONLINE_NW, false, false>(a, grid, check, stream);
     if (st) return st;
   }
   return ok();

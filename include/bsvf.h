@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BSVF_ABI_VERSION 4
+#define BSVF_ABI_VERSION 5
 
 /* Status codes. */
 enum {
@@ -79,10 +79,17 @@ enum {
                                     2 * scale * max|q| over its rows * max|k|
                                     over its attended keys <= ATTN_ELIGIBLE_NATS,
                                     else the running max */
-  ATTN_SOFTMAX_BOUND_EXACT = 4   /* as ATTN_SOFTMAX_BOUND, but no head uses the
+  ATTN_SOFTMAX_BOUND_EXACT = 4,  /* as ATTN_SOFTMAX_BOUND, but no head uses the
                                     prescaled Q of ATTN_PRESCALE_NATS: every
                                     bound head scales each score instead
                                     (slower, Q never rounded) */
+  ATTN_SOFTMAX_BOUND_CHECKED = 5 /* as ATTN_SOFTMAX_BOUND_TILE, and a tile whose
+                                    bound lies in (ATTN_ELIGIBLE_NATS,
+                                    ATTN_CHECK_NATS] runs with the bound shift
+                                    as well (Q exact), then keeps the result
+                                    iff every row's l >= 2^ATTN_CHECK_LOG2_L;
+                                    else it is computed again with the
+                                    running max */
 };
 
 /* Values written to head_path_out. */
@@ -103,6 +110,20 @@ enum { ATTN_PATH_ONLINE = 0, ATTN_PATH_BOUND = 1 };
  * score (the rounding moves a score by up to 2^-9 of scale*|q||k|, which
  * matters only for large logits).  Both use the same fixed shift. */
 #define ATTN_PRESCALE_NATS 40.0f
+
+/* ATTN_SOFTMAX_BOUND_CHECKED: tiles whose slack bound exceeds
+ * ATTN_ELIGIBLE_NATS but not ATTN_CHECK_NATS try the bound shift and check it
+ * after the fact.  The shift never lies below a score, so the one way it can
+ * fail is underflow.  Terms exp(s_ij - m_i) below the normal float32/bf16
+ * range (2^-126) are lost or denormal; over n keys they change l and the
+ * output's numerator by less than n * 2^-126.  A row that keeps
+ * l >= 2^ATTN_CHECK_LOG2_L therefore loses less than n * 2^-26 of it
+ * (2^-12 at 16,384 keys, and only if nearly every term sits just below the
+ * range).  A tile with a row below the limit is computed again with the
+ * running max; its first result is discarded, at the cost of a second pass
+ * over the tile's keys. */
+#define ATTN_CHECK_NATS 256.0f
+#define ATTN_CHECK_LOG2_L (-100.0f)
 
 /* Frame-window pattern (host struct). */
 typedef struct attn_pattern_t {
@@ -284,9 +305,11 @@ typedef struct attn_blocks_t {
  *       products and norms).  Heads (tiles, mode 3) whose slack bound is at
  *       most ATTN_PRESCALE_NATS (except in mode 4), and every head in mode 2,
  *       use Q multiplied by scale*log2(e) and rounded to bf16 once; the rest
- *       use Q as given.
+ *       use Q as given.  In mode 5 a tile that fails its check is computed
+ *       twice, and its outputs are those of the second (running max) pass.
  *   head_path_out: device int32 [B][H] or NULL; receives ATTN_PATH_* per head
- *       (for ATTN_SOFTMAX_BOUND_TILE: the path of the head's first tile).
+ *       (for ATTN_SOFTMAX_BOUND_TILE and _CHECKED: the path of the head's
+ *       first tile, after its check).
  * Errors: ATTN_E_INVAL (NULL tensor or block pointers, non-positive sizes,
  * bad mode, bad scale), ATTN_E_ALIGN (N % 16, block_q % 16, misaligned pointer
  * or stride), ATTN_E_UNSUPPORTED (D not 64/128, block_q > ATTN_MAX_BLOCK_Q,
@@ -348,6 +371,7 @@ int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float
  * summation order.  Requires tokens_per_frame >= 64, global frames below 64,
  * and a list built with a granule that is a multiple of 64 (each 64-key stage
  * then lies in one run); ATTN_E_UNSUPPORTED / ATTN_E_PATTERN otherwise.
+ * Softmax modes 0 to 4 (ATTN_SOFTMAX_BOUND_CHECKED: ATTN_E_UNSUPPORTED).
  */
 int attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
                     float* shift_out, int32_t batch, int32_t heads, int32_t seq_len,

@@ -14,6 +14,7 @@ tiny       1       2      64    4 x 48   (N 192)    +-1 frame
 720p       1       8      128   13 x 3600 (N 46800) +-1 frame + frame 0 global
 1080p      1       8      128   7 x 8160 (N 57120)  +-1 frame + frame 0 global
 stress     as 720p, rows scaled by log-normal(0, 0.75) norms, 1% of keys x8
+spread     as 720p, rows scaled by log-normal(0, 0.25) norms, no outliers
 hotframe   as 720p, the Q and K rows of frame 6 doubled
 sr         1       16     64    5 x 14400 (N 72000) frame-local
 =========  ======  =====  ====  ==================  ==========================
@@ -25,6 +26,9 @@ Q, K, V first, then ``z_q``, ``z_k`` (``[B, H, N]`` standard normal) and an
 outlier uniform ``[B, H, N]``; each Q row is multiplied by ``exp(0.75 z_q)``,
 each K row by ``exp(0.75 z_k)`` and, where the uniform is below 0.01, by 8;
 all in float32, rounded to bf16 once at the end.  V is left unscaled.  The
+spread workload is the same construction with sigma 0.25 and no outliers:
+every head's norm certificate exceeds the eligibility limit, while the true
+slack of its rows stays far below it.  The
 hotframe workload takes the 720p Q and K and doubles every row of frame 6
 (exact in bf16): per-head eligibility then fails on every head, while the
 tiles whose keys avoid frame 6 stay eligible.
@@ -69,6 +73,7 @@ class Workload:
     pattern: Pattern
     stress: bool = False
     seed: int = 0
+    stress_params: tuple = (0.75, 0.01, 8.0)   # (sigma, outlier rate, outlier scale)
     hot_frame: tuple = ()   # (frame, factor): Q and K rows of that frame scaled
 
     @property
@@ -88,6 +93,8 @@ WORKLOADS = {
     "stress": Workload("stress", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), stress=True),
     "sr": Workload("sr", 1, 16, 64, Pattern(5, 14400, 0, 0)),
     "hotframe": Workload("hotframe", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), hot_frame=(6, 2.0)),
+    "spread": Workload("spread", 1, 8, 128, Pattern(13, 3600, 1, 1, (0,)), stress=True,
+                       stress_params=(0.25, 0.0, 8.0)),
 }
 
 
@@ -100,6 +107,7 @@ FRAME_GRID = {
     "stress": (45, 80),
     "sr": (90, 160),
     "hotframe": (45, 80),
+    "spread": (45, 80),
 }
 
 
@@ -154,7 +162,7 @@ def random_qkv(batch, heads, seq_len, head_dim, seed=0, stress=False, stress_par
 def make_qkv(wl: Workload, seed: int | None = None):
     """Q, K, V bf16 bit arrays for a named workload."""
     q, k, v = random_qkv(wl.batch, wl.heads, wl.seq_len, wl.head_dim,
-                         wl.seed if seed is None else seed, wl.stress)
+                         wl.seed if seed is None else seed, wl.stress, wl.stress_params)
     if wl.hot_frame:
         f, c = wl.hot_frame
         T = wl.pattern.tokens_per_frame

@@ -231,7 +231,9 @@ def fwd_call(entry="attn_fwd", **over):
     (dict(blocks=None), 1),
     (dict(strides=None), 1),
     (dict(B=0), 1),
-    (dict(mode=5), 1),                     # no such mode
+    (dict(mode=6), 1),                     # no such mode
+    (dict(mode=-1), 1),                    # no such mode
+    (dict(mode=5), 5),                     # checked bound without norms
     (dict(mode=4), 5),                     # exact bound without norms
     (dict(mode=3), 5),                     # per-tile bound without norms
     (dict(scale=0.0), 1),
@@ -454,3 +456,17 @@ def test_device_blocks_orders_calls_across_streams():
         st.order_on(s)
     assert log == []
 
+
+
+@no_gpu_only
+def test_masked_entry_rejects_the_checked_mode():
+    """attn_fwd_masked takes softmax modes 0 to 4: mode 5 is refused before any
+    device work (ATTN_E_UNSUPPORTED), mode 6 as no mode at all."""
+    L = bs.lib()
+    pat = bs._Pattern(4, 48, 1, 1, 0, None)
+    st = (ctypes.c_int64 * 12)(*([192 * 64 * 2, 192 * 64, 64] * 4))
+    cb = bs._Blocks(FAKE, FAKE, FAKE, 4, 4, 256, None, 0)
+    for mode, want in ((5, 5), (6, 1)):
+        got = L.attn_fwd_masked(FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 192, 64, st, ctypes.c_float(0.125),
+                                ctypes.byref(cb), FAKE, ctypes.byref(pat), FAKE, FAKE, FAKE, mode, None, None)
+        assert got == want, (mode, got, bs.lib().attn_last_error())

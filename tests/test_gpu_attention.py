@@ -41,6 +41,14 @@ def oracle_rows(name, rows):
     return _ORACLE[key]
 
 
+def out_scale(name, O):
+    """1, or for the spread and hotframe inputs max(1, |O_ref|) per element:
+    their large-norm rows attend sharply and reach |O| of 2-4, where half an
+    ulp of the bf16 output alone is 0.008 (0.016 above 4), so the absolute
+    bound is scaled there, as for the other peaked inputs."""
+    return np.maximum(1.0, np.abs(O)) if name in ("spread", "hotframe") else 1.0
+
+
 def rows_for(name):
     wl = WORKLOADS[name]
     blk = bs.build_blocks_for(wl.pattern, 256)
@@ -78,7 +86,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
-@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4, 5])
 def test_small_all_rows(case, mode):
     p, B, H, D, bq = SMALL[case]
     q, k, v = random_qkv(B, H, p.seq_len, D, seed=100 + case)
@@ -100,7 +108,8 @@ def test_workload_sampled_rows(name, mode):
     rows = rows_for(name)
     res = run_gpu(q, k, v, wl.pattern, wl.scale, mode)
     O, L = oracle_rows(name, rows)
-    e = errors(res["o"][:, :, rows], res["lse"][:, :, rows], O, L)
+    s = out_scale(name, O)
+    e = errors(res["o"][:, :, rows] / s, res["lse"][:, :, rows], O / s, L)
     print(name, mode, e)
     record("workload_sampled_rows", name, mode, e)
     assert within(e), e
@@ -544,3 +553,111 @@ def test_persistent_launch_any_queue_layout(num_xcd, group, mode):
         assert o.contiguous().view(torch.int16).cpu().numpy().tobytes() == ref["o_bytes"]
         assert lse.cpu().numpy().tobytes() == ref["lse_bytes"]
         assert not blk.work_ctr.cpu().numpy().any()
+
+
+def _checked_inputs(D):
+    """Rows scaled by exp(0.25 z) (the spread construction), and frame 3's Q
+    rows tripled: the tiles' certificates lie between 50 and 350 nats; most
+    checked tiles keep the bound, frame 3's fail or exceed the check limit."""
+    p = Pattern(6, 272, 1, 1, (0,))   # 256 + 16 rows per frame: full and thin tiles
+    q, k, v = random_qkv(1, 2, p.seq_len, D, seed=41, stress=True, stress_params=(0.25, 0.0, 8.0))
+    T = p.tokens_per_frame
+    f = OA.widen(q).astype(np.float32)
+    f[:, :, 3 * T:4 * T] *= np.float32(3.0)
+    return p, f32_to_bf16_bits(f), k, v
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_checked_tiles(D):
+    """Softmax mode 5 against the oracle's checked per-tile test: all rows
+    within the band; per tile, the shift the kernel used is the bound (tiles
+    the certificate or the check keeps) or the row max (tiles beyond the check
+    limit, and checked tiles some row of which has l < 2^-100, which run
+    again); bitwise the same run to run and in the static launch."""
+    p, q, k, v = _checked_inputs(D)
+    B, H = q.shape[:2]
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    res = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND_CHECKED, repeat=2)
+    O, L = OA.attention(q, k, v, p, scale)
+    # frame 3's rows attend sharply (|O| up to about 3): the absolute bound is
+    # scaled by max(1, |O_ref|) per element, as for the per-tile test
+    s = np.maximum(1.0, np.abs(O))
+    e = errors(res["o"] / s, res["lse"], O / s, L)
+    record("checked_tiles", f"D{D}", 5, e)
+    assert within(e), e
+    blk = bs.build_blocks_for(p, 256)
+    tiles = [tuple(map(int, t)) for t in blk.q_tiles]
+    paths, min_ln_l = ON.checked_tile_paths(q, k, v, p, scale, tiles)
+    cert = ON.tile_slack_bound(q, k, p, scale, tiles)
+    # every kind of tile occurs, and no decision sits near a threshold
+    assert {0, 1, 2} <= set(paths.ravel().tolist())
+    assert ((paths == 0) & ~np.isnan(min_ln_l)).any()              # checked, then run again
+    limit = bs.CHECK_LOG2_L * math.log(2.0)
+    near = np.abs(min_ln_l - limit) < 2.0
+    assert not near.any()
+    # (a certificate near ELIGIBLE_NATS decides only between certified and
+    # checked, and both keep the bound on these tiles)
+    assert (np.abs(cert - ON.CHECK_NATS) > 2.0).all()
+    mx = OA.scores_max(q, k, p, scale)
+    bd = ON.row_bound(q, k, p, scale)
+    for t, (qs, nr) in enumerate(tiles):
+        sl = slice(qs, qs + nr)
+        for b in range(B):
+            for h in range(H):
+                shift = res["shift"][b, h, sl]
+                if paths[b, h, t]:
+                    assert (shift >= mx[b, h, sl]).all()
+                    assert (np.abs(shift - bd[b, h, sl] * (1 + 2.0 ** -8)) <= 1e-5 * np.maximum(bd[b, h, sl], 1)).all()
+                else:
+                    assert (np.abs(shift - mx[b, h, sl]) <= 1e-3 * np.maximum(np.abs(mx[b, h, sl]), 1)).all()
+    want_hp = np.where(paths[:, :, 0] > 0, bs.PATH_BOUND, bs.PATH_ONLINE)
+    assert np.array_equal(res["head_path"], want_hp)
+    again = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND_CHECKED)
+    static = run_gpu(q, k, v, p, scale, bs.SOFTMAX_BOUND_CHECKED, persistent=False)
+    for r in (again, static):
+        assert r["o_bytes"] == res["o_bytes"] and r["lse_bytes"] == res["lse_bytes"]
+
+
+@pytest.mark.parametrize("name", ["spread", "stress", "720p", "hotframe"])
+def test_checked_workloads(name):
+    """Mode 5 at full size on sampled rows: within the band; per tile, the
+    sampled rows all used the bound (times 1 + 2^-8) or all the row max;
+    tiles whose certificate passes keep the bound, tiles beyond the check
+    limit take the row max, and a tile with a sampled row whose l under the
+    bound is below 2^-100 (by more than 2 nats) was run again."""
+    wl = WORKLOADS[name]
+    q, k, v = inputs(name)
+    rows = rows_for(name)
+    res = run_gpu(q, k, v, wl.pattern, wl.scale, bs.SOFTMAX_BOUND_CHECKED)
+    O, L = oracle_rows(name, rows)
+    s = out_scale(name, O)
+    e = errors(res["o"][:, :, rows] / s, res["lse"][:, :, rows], O / s, L)
+    record("checked_workloads", name, 5, e)
+    assert within(e), e
+    blk = bs.build_blocks_for(wl.pattern, 256)
+    tiles = [tuple(map(int, t)) for t in blk.q_tiles]
+    cert = ON.tile_slack_bound(q, k, wl.pattern, wl.scale, tiles)
+    bd = ON.row_bound(q, k, wl.pattern, wl.scale, rows=rows)
+    mx = OA.scores_max(q, k, wl.pattern, wl.scale, rows=rows)
+    ln_l = L - bd
+    limit = bs.CHECK_LOG2_L * math.log(2.0)
+    kept = np.zeros(cert.shape, dtype=bool)
+    tile_of = np.searchsorted(np.array([t[0] for t in tiles]), rows, side="right") - 1
+    for t in range(len(tiles)):
+        idx = np.nonzero(tile_of == t)[0]
+        for b in range(wl.batch):
+            for h in range(wl.heads):
+                sh = res["shift"][b, h, rows[idx]]
+                on_bound = np.abs(sh - bd[b, h, idx] * (1 + 2.0 ** -8)) <= 1e-5 * np.maximum(bd[b, h, idx], 1)
+                on_max = np.abs(sh - mx[b, h, idx]) <= 1e-3 * np.maximum(np.abs(mx[b, h, idx]), 1)
+                assert on_bound.all() or on_max.all()
+                kept[b, h, t] = on_bound.all()
+                if cert[b, h, t] <= ON.ELIGIBLE_NATS - 0.5:
+                    assert kept[b, h, t]
+                if cert[b, h, t] > ON.CHECK_NATS + 2.0 or (ln_l[b, h, idx] < limit - 2.0).any():
+                    assert not kept[b, h, t]
+    print(name, "tiles on the bound:", kept.mean())
+    if name == "spread":       # nearly every certificate fails, and the check keeps nearly every tile
+        assert (cert > ON.ELIGIBLE_NATS).mean() > 0.99 and kept.mean() > 0.9
+    if name == "stress":       # certificates far beyond the check limit
+        assert not kept.any()

@@ -352,3 +352,23 @@ def test_checked_tile_paths_reduce_to_the_tile_test():
     assert (cert <= NM.ELIGIBLE_NATS).all()
     paths, min_ln_l = NM.checked_tile_paths(q, k, v, p, 0.125, tiles)
     assert (paths == 1).all() and np.isnan(min_ln_l).all()
+
+
+def test_spread_recipe():
+    """The spread input is the stress construction with sigma 0.25 and no
+    outliers on the 720p shape: every Q and K row of the N(0,1) draw scaled by
+    exp(0.25 z), z drawn after Q, K, V; shown on a small shape against the
+    recipe written out."""
+    import dataclasses
+    from synth import f32_to_bf16_bits
+    sp = WORKLOADS["spread"]
+    assert dataclasses.replace(sp, name="720p", stress=False, stress_params=(0.75, 0.01, 8.0)) == WORKLOADS["720p"]
+    assert sp.stress and sp.stress_params == (0.25, 0.0, 8.0)
+    q, k, v = random_qkv(1, 2, 64, 16, seed=3, stress=True, stress_params=(0.25, 0.0, 8.0))
+    rng = np.random.default_rng(3)
+    draw = lambda shape: rng.standard_normal(size=shape, dtype=np.float32)
+    q0, k0, v0 = draw((1, 2, 64, 16)), draw((1, 2, 64, 16)), draw((1, 2, 64, 16))
+    zq, zk = draw((1, 2, 64)), draw((1, 2, 64))
+    assert np.array_equal(q, f32_to_bf16_bits(q0 * np.exp(np.float32(0.25) * zq)[..., None]))
+    assert np.array_equal(k, f32_to_bf16_bits(k0 * np.exp(np.float32(0.25) * zk)[..., None]))
+    assert np.array_equal(v, f32_to_bf16_bits(v0))
