@@ -136,8 +136,9 @@ def time_producer(bs, wl, q, k, dev, steps: int, warmup: int):
 
 def time_modes(bs, wl, dev, steps: int, warmup: int, modes=(0, 1), tensors=None):
     """attn_fwd per softmax mode on one workload, each timed by events on the
-    launch stream over `steps` calls after `warmup`; the bound modes also time
-    attn_norms, which their step includes.  Returns {mode: (fwd_ms, norms_ms)}
+    launch stream over about `steps` calls (interleaved with the other modes,
+    in 4 rounds) after `warmup` each; the bound modes also time attn_norms,
+    which their step includes.  Returns {mode: (fwd_ms, norms_ms)}
     and the head paths of the mode-1 call."""
     import torch
     from synth import make_qkv
@@ -157,33 +158,44 @@ def time_modes(bs, wl, dev, steps: int, warmup: int, modes=(0, 1), tensors=None)
     lse = torch.empty(B, H, N, dtype=torch.float32, device=dev)
     hp = torch.zeros(B, H, dtype=torch.int32, device=dev)
     out, paths = {}, None
-    for mode in modes:
+
+    def run(mode, ev=None):
         bound = mode != bs.SOFTMAX_ONLINE
-
-        def run(ev=None):
-            if bound:
-                if ev:
-                    ev[0].record()
-                bs.norms(q, k, out=nm)
+        if bound:
             if ev:
-                ev[1].record()
-            bs.attention(q, k, v, dblk, wl.scale, mode, norms=nm if bound else None, out=o, lse=lse,
-                         head_path=hp)
-            if ev:
-                ev[2].record()
+                ev[0].record()
+            bs.norms(q, k, out=nm)
+        if ev:
+            ev[1].record()
+        bs.attention(q, k, v, dblk, wl.scale, mode, norms=nm if bound else None, out=o, lse=lse,
+                     head_path=hp)
+        if ev:
+            ev[2].record()
 
+    # The modes are timed interleaved, in rounds, so that a clock that is
+    # still rising after the input upload (or falling with heat) weighs on
+    # all of them alike rather than on the first.
+    for mode in modes:
         for _ in range(warmup):
-            run()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for e in evs:
-            run(e)
-        torch.cuda.synchronize()
-        fwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-        nms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if bound else 0.0
+            run(mode)
+    rounds = 4
+    per = max(1, steps // rounds)
+    evs = {mode: [] for mode in modes}
+    torch.cuda.synchronize()
+    for _ in range(rounds):
+        for mode in modes:
+            for _ in range(per):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                run(mode, e)
+                evs[mode].append(e)
+    torch.cuda.synchronize()
+    if bs.SOFTMAX_BOUND in modes:
+        run(bs.SOFTMAX_BOUND)
+        paths = hp.cpu().tolist()
+    for mode in modes:
+        fwd = float(np.mean([e[1].elapsed_time(e[2]) for e in evs[mode]]))
+        nms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs[mode]])) if mode != bs.SOFTMAX_ONLINE else 0.0
         out[mode] = (fwd, nms)
-        if mode == bs.SOFTMAX_BOUND:
-            paths = hp.cpu().tolist()
     return out, paths, 4.0 * D * blocks.useful_pairs * B * H
 
 

@@ -279,51 +279,48 @@ int attn_build_schedule(const int32_t* q_tiles, const int32_t* kv_ptr, const int
     // Tiles of one (batch, head) with the same key intervals (the tiles of one
     // query frame) read the same K and V: keep each such set together on one
     // die, so its tiles stream those keys through that die's L2 at the same
-    // time.  Sets go, heaviest first, to the die with the least work so far.
-    // Short tiles stay out of the sets: dealt last, heaviest first, each to
-    // the die with the least work, they even out the ends of the queues.
-    struct Set { int64_t cost; std::vector<int32_t> items; };
-    std::vector<Set> sets;
-    std::vector<int32_t> fill;
+    // time.  Sets of neighbouring frames share most of their keys (the
+    // window, the global frames), so the sets in (batch, head, frame) order
+    // are cut into num_xcd contiguous runs of about equal cost: a die works
+    // through whole heads, or long stretches of one, frame after frame.
+    // Short tiles stay out of the sets (a walk of few rows runs ahead of the
+    // set's full tiles and would fetch the keys alone): each goes to its
+    // set's die, after all of that die's sets, in the same order, where the
+    // short tiles of neighbouring frames run together.
+    struct Unit { int64_t cost; std::vector<int32_t> items, shorts; };
+    std::vector<Unit> units;
+    int64_t total = 0;
     for (int64_t bh = 0; bh < (int64_t)batch * heads; ++bh) {
       int32_t t = 0;
       while (t < n_qt) {
-        Set st{0, {}};
+        Unit un{0, {}, {}};
         int32_t u = t;
         for (; u < n_qt; ++u) {
           const int32_t n0 = kv_ptr[t + 1] - kv_ptr[t], n1 = kv_ptr[u + 1] - kv_ptr[u];
           if (n0 != n1 || !std::equal(kv_iv + 2 * kv_ptr[t], kv_iv + 2 * kv_ptr[t + 1], kv_iv + 2 * kv_ptr[u]))
             break;
-          if (is_short[u]) {
-            fill.push_back((int32_t)(bh * n_qt + u));
-          } else {
-            st.items.push_back((int32_t)(bh * n_qt + u));
-            st.cost += cost[u];
-          }
+          (is_short[u] ? un.shorts : un.items).push_back((int32_t)(bh * n_qt + u));
+          un.cost += cost[u];
         }
-        if (!st.items.empty()) sets.push_back(std::move(st));
+        total += un.cost;
+        units.push_back(std::move(un));
         t = u;
       }
     }
-    std::stable_sort(sets.begin(), sets.end(), [](const Set& a, const Set& b) { return a.cost > b.cost; });
-    std::stable_sort(fill.begin(), fill.end(), [&](int32_t a, int32_t b) { return cost[a % n_qt] > cost[b % n_qt]; });
-    std::vector<int64_t> load(num_xcd, 0);
-    auto least = [&]() {
+    // unit j goes to the die whose share of the total cost holds its midpoint
+    std::vector<std::vector<int32_t>> tail(num_xcd);
+    int64_t before = 0;
+    for (const Unit& un : units) {
       int x = 0;
-      for (int j = 1; j < num_xcd; ++j)
-        if (load[j] < load[x]) x = j;
-      return x;
-    };
-    for (const Set& st : sets) {
-      const int x = least();
-      load[x] += st.cost;
-      queue[x].insert(queue[x].end(), st.items.begin(), st.items.end());
+      if (total > 0) {
+        const long double mid = (long double)before + (long double)un.cost / 2;
+        x = (int)std::min<long double>(num_xcd - 1, mid * num_xcd / total);
+      }
+      before += un.cost;
+      queue[x].insert(queue[x].end(), un.items.begin(), un.items.end());
+      tail[x].insert(tail[x].end(), un.shorts.begin(), un.shorts.end());
     }
-    for (int32_t w : fill) {
-      const int x = least();
-      load[x] += cost[w % n_qt];
-      queue[x].push_back(w);
-    }
+    for (int x = 0; x < num_xcd; ++x) queue[x].insert(queue[x].end(), tail[x].begin(), tail[x].end());
   }
   size_t depth = 0;
   for (const auto& q : queue) depth = std::max(depth, q.size());

@@ -203,10 +203,13 @@ int attn_build_blocks_granular(const attn_pattern_t* p, int32_t granule, int32_t
  *     j % num_xcd;
  *   group == 0: the tiles of one (batch, head) that share their key
  *     intervals (one query frame's tiles) form a set that stays together on
- *     one die, so they stream the same K and V through that die's L2; sets,
- *     heaviest first, go to the die with the least cost so far.  Short tiles
- *     are left out of the sets and dealt after them, heaviest first, each to
- *     the die with the least cost so far.
+ *     one die, so they stream the same K and V through that die's L2.  The
+ *     sets, in (batch, head, frame) order, are cut into num_xcd contiguous
+ *     runs of about equal cost (a set goes to the die whose share of the
+ *     total cost holds the middle of the set's cost), so neighbouring frames,
+ *     which share most of their keys, run on one die.  Short tiles are left
+ *     out of their sets and follow all of their die's sets, in the same
+ *     order.
  * Queues are padded with -1 to a common depth (a multiple of `group` when
  * group > 0); such a workgroup exits at once.  The result is a permutation of
  * all items plus padding; it changes only the execution order, never results.

@@ -140,9 +140,11 @@ def test_schedule_is_a_padded_permutation(name):
 @pytest.mark.parametrize("block_q", [256, 64])
 def test_frame_set_schedule(name, block_q):
     """group 0: a permutation; each set of tiles with equal key intervals of one
-    head (short tiles left out) sits contiguously on a single die; the short
-    tiles come after every set, heaviest first; die loads end within the
-    largest set or short tile of each other."""
+    head (short tiles left out) sits contiguously on a single die; the sets go
+    to the dies in (head, frame) order, each die taking a contiguous run; the
+    short tiles follow every set of their die, in the same order, each on its
+    set's die; die loads end within the largest set (with its short tiles) of
+    each other."""
     wl = WORKLOADS[name]
     blk = bs.build_blocks_for(wl.pattern, block_q)
     items = blk.n_qt * wl.heads * wl.batch
@@ -157,6 +159,7 @@ def test_frame_set_schedule(name, block_q):
     cost = _tile_costs(blk)
     loads = []
     seen = set()
+    firsts = []
     for x in range(xcd):
         q = [w for w in order[x::xcd] if w >= 0]
         assert all(w == -1 for w in order[x::xcd][len(q):])       # padding only at the end
@@ -164,8 +167,7 @@ def test_frame_set_schedule(name, block_q):
         flags = [short[w % blk.n_qt] for w in q]
         n_long = flags.count(False)
         assert not any(flags[:n_long])                            # short tiles after the sets
-        tail = [cost[w % blk.n_qt] for w in q[n_long:]]
-        assert all(a >= b for a, b in zip(tail, tail[1:]))        # heaviest first
+        assert q[:n_long] == sorted(q[:n_long]) and q[n_long:] == sorted(q[n_long:])   # (head, frame) order
         runs = []
         for w in q[:n_long]:
             s = (w // blk.n_qt, key[w % blk.n_qt])
@@ -174,10 +176,18 @@ def test_frame_set_schedule(name, block_q):
         assert len(runs) == len(set(runs))                        # each set contiguous
         assert not (set(runs) & seen)                             # and on one die only
         seen |= set(runs)
+        firsts.append(q[0] if q else None)
+        for w in q[n_long:]:                                      # a short tile on its set's die
+            t = w % blk.n_qt
+            same = [u for u in range(blk.n_qt) if key[u] == key[t] and not short[u]]
+            assert not same or (w // blk.n_qt, key[t]) in set(runs)
+    # the dies' runs follow one another in (head, frame) order
+    nonempty = [f for f in firsts if f is not None]
+    assert nonempty == sorted(nonempty)
     units = {}
     for w in range(items):
         t = w % blk.n_qt
-        u = ("short", w) if short[t] else (w // blk.n_qt, key[t])
+        u = (w // blk.n_qt, key[t])
         units[u] = units.get(u, 0) + cost[t]
     assert max(loads) - min(loads) <= max(units.values())
 
