@@ -286,7 +286,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="720p")
-    ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with per-head fallback, 2 forced bound, 3 bound per query tile")
+    ap.add_argument("--mode", type=int, default=1, help="0 online, 1 bound with per-head fallback, 2 forced bound, "
+                    "3 bound per query tile, 4 as 1 with Q never rounded, 5 as 3 with the checked test")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", default="aligned16", choices=["aligned16", "granular128"],

@@ -25,7 +25,7 @@ import numpy as np
 __all__ = [
     "SOFTMAX_ONLINE", "SOFTMAX_BOUND", "SOFTMAX_BOUND_FORCED", "SOFTMAX_BOUND_TILE", "SOFTMAX_BOUND_EXACT",
     "SOFTMAX_BOUND_CHECKED", "PATH_ONLINE", "PATH_BOUND",
-    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "PRESCALE_NATS", "CHECK_NATS", "CHECK_LOG2_L", "AttnError", "lib", "library_path", "abi_version",
+    "MAX_BLOCK_Q", "ELIGIBLE_NATS", "PRESCALE_NATS", "CHECK_NATS", "CHECK_LOG2_L", "CHECK_SHIFT_NATS", "AttnError", "lib", "library_path", "abi_version",
     "Blocks", "DeviceBlocks", "build_blocks", "build_blocks_granular", "build_schedule", "norms", "qk_prep",
     "attention",
 ]
@@ -38,6 +38,7 @@ ELIGIBLE_NATS = 60.0
 PRESCALE_NATS = 40.0
 CHECK_NATS = 256.0
 CHECK_LOG2_L = -100.0
+CHECK_SHIFT_NATS = 40.0
 ABI_VERSION = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -45,6 +45,7 @@
 #include "bsvf_device.h"
 #include "bsvf_internal.h"
 
+#include <cfloat>
 #include <mutex>
 
 namespace bsvf {
@@ -71,6 +72,8 @@ constexpr float kBoundMargin = 1.0f + 1.0f / 256.0f;
 // Smallest row sum a checked tile keeps (2^ATTN_CHECK_LOG2_L).
 constexpr float kCheckMinL = 0x1p-100f;
 static_assert(ATTN_CHECK_LOG2_L == -100.0f, "kCheckMinL is 2^ATTN_CHECK_LOG2_L");
+// A checked tile's shift lies ATTN_CHECK_SHIFT_NATS below the bound (log2 units).
+constexpr float kCheckShift2 = ATTN_CHECK_SHIFT_NATS * kLog2e;
 // Bound rows come in two kinds.  Where the slack bound is at most
 // ATTN_PRESCALE_NATS, the bound loop keeps Q multiplied by scale*log2(e) and
 // rounded to bf16 once, and starts the score accumulator at -m, so the MFMA
@@ -1266,6 +1269,9 @@ __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, c
     if (BOUND || T.fixed) {
       const float qn = q_norm[(int64_t)bh * a.N + qs + (valid ? r : 0)];
       T.m2[qb] = valid ? qn * kfac * kLog2e : 0.0f;
+      if constexpr (CHECK) {
+        if (path == kCheck) T.m2[qb] -= kCheckShift2;
+      }
     } else {
       T.m2[qb] = -INFINITY;
     }
@@ -1299,7 +1305,10 @@ __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, c
     // Mode 5 checks every tile that ran with a fixed shift (kExact or
     // kCheck; a kExact tile always passes, its certificate keeps l above
     // e^-ATTN_ELIGIBLE_NATS).  Both conditions are re-read rather than kept
-    // in a register across the walk.
+    // in a register across the walk.  A row passes when its l is at least
+    // 2^ATTN_CHECK_LOG2_L and finite and its accumulator finite (a kCheck
+    // shift lies below the bound, so terms up to e^ATTN_CHECK_SHIFT_NATS
+    // occur).
     if (T.fixed && a.mode == ATTN_SOFTMAX_BOUND_CHECKED) {
       // Every row's full l (both lane halves; after a thin walk, held by the
       // first wave of each row group) against 2^ATTN_CHECK_LOG2_L.
@@ -1309,7 +1318,12 @@ __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, c
         for (int qb = 0; qb < NQB; ++qb) {
           const float lh = T.lsum[qb] + T.lsum2[qb];
           const float lt = lh + __shfl_xor(lh, 32);
-          low |= row0 + qb * 32 + T.n < nr && !(lt >= kCheckMinL);
+          bool ok = lt >= kCheckMinL && lt <= FLT_MAX;
+#pragma unroll
+          for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ok = ok && __builtin_isfinite(T.oacc[qb][db][r]);
+          low |= row0 + qb * 32 + T.n < nr && !ok;
         }
       }
       if (group_any<NW>(__any(low), smem, wv, lane)) return kRetry;

@@ -85,11 +85,12 @@ enum {
                                     (slower, Q never rounded) */
   ATTN_SOFTMAX_BOUND_CHECKED = 5 /* as ATTN_SOFTMAX_BOUND_TILE, and a tile whose
                                     bound lies in (ATTN_ELIGIBLE_NATS,
-                                    ATTN_CHECK_NATS] runs with the bound shift
-                                    as well (Q exact), then keeps the result
-                                    iff every row's l >= 2^ATTN_CHECK_LOG2_L;
-                                    else it is computed again with the
-                                    running max */
+                                    ATTN_CHECK_NATS] runs with the bound less
+                                    ATTN_CHECK_SHIFT_NATS as a fixed shift
+                                    (Q exact), then keeps the result iff
+                                    every row's l >= 2^ATTN_CHECK_LOG2_L and
+                                    nothing overflowed; else it is computed
+                                    again with the running max */
 };
 
 /* Values written to head_path_out. */
@@ -112,18 +113,21 @@ enum { ATTN_PATH_ONLINE = 0, ATTN_PATH_BOUND = 1 };
 #define ATTN_PRESCALE_NATS 40.0f
 
 /* ATTN_SOFTMAX_BOUND_CHECKED: tiles whose slack bound exceeds
- * ATTN_ELIGIBLE_NATS but not ATTN_CHECK_NATS try the bound shift and check it
- * after the fact.  The shift never lies below a score, so the one way it can
- * fail is underflow.  Terms exp(s_ij - m_i) below the normal float32/bf16
- * range (2^-126) are lost or denormal; over n keys they change l and the
- * output's numerator by less than n * 2^-126.  A row that keeps
+ * ATTN_ELIGIBLE_NATS but not ATTN_CHECK_NATS run with the shift
+ * m_i - ATTN_CHECK_SHIFT_NATS (m_i the bound) and check it after the fact.
+ * Every term exp(s_ij - m_i') is then at most e^ATTN_CHECK_SHIFT_NATS, so l
+ * and the accumulators stay finite unless |v| exceeds about e^38 / n; the
+ * check tests that anyway.  Terms below the normal float32/bf16 range
+ * (2^-126) are lost or denormal; over n keys they change l and the output's
+ * numerator by less than n * 2^-126.  A row that keeps
  * l >= 2^ATTN_CHECK_LOG2_L therefore loses less than n * 2^-26 of it
  * (2^-12 at 16,384 keys, and only if nearly every term sits just below the
- * range).  A tile with a row below the limit is computed again with the
+ * range).  A tile with a row outside those limits is computed again with the
  * running max; its first result is discarded, at the cost of a second pass
  * over the tile's keys. */
 #define ATTN_CHECK_NATS 256.0f
 #define ATTN_CHECK_LOG2_L (-100.0f)
+#define ATTN_CHECK_SHIFT_NATS 40.0f
 
 /* Frame-window pattern (host struct). */
 typedef struct attn_pattern_t {
@@ -294,7 +298,8 @@ typedef struct attn_blocks_t {
  *       (d-stride 1 for all four).
  *   lse: device fp32 [B][H][N] contiguous, or NULL.
  *   shift_out: device fp32 [B][H][N] or NULL; receives the shift m_i used by
- *       the row (natural-log units; the bound itself on bound heads).
+ *       the row (natural-log units; the bound itself on bound heads, the
+ *       bound less ATTN_CHECK_SHIFT_NATS on tiles kept by the check).
  *   scale: softmax scale (usually 1/sqrt(D)); must be > 0 and finite.
  *   blocks: block list (see attn_blocks_t).  It must come from
  *       attn_build_blocks for this N; the kernel skips any tile or interval
