@@ -115,6 +115,7 @@ struct FwdArgs {
   const float* k_gmax;
   const float* head_max;
   int32_t mode;
+  int32_t gate;             // persistent online-only launch: kGateNone or kGateOnline
   int32_t* head_path_out;
   // frame mask of the frame-unaware layout (kernels built with MASK only)
   const int32_t* kv_flag;   // per interval: 1 = some (row, key) pair masked
@@ -1133,6 +1134,19 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const ci32* kv_iv, u1
 // What run_item did with an item.
 enum ItemResult { kDeclined = 0, kDone = 1, kRetry = 2 };
 
+// The per-head test's slack bound of head bh in nats: the largest score any
+// of its rows can reach, 2 * scale * max|q| * max|k| (twice the largest
+// possible distance between the shift and a score).
+__device__ __forceinline__ float head_slack(float scale, const cf32* head_max, int bh) {
+  return 2.0f * scale * head_max[2 * bh] * head_max[2 * bh + 1];
+}
+
+// In the per-head mode the persistent launch is two kernels on the same
+// work: the online-only kernel, which has a register allocation of its own,
+// then the combined kernel (both loops).  The first (kGateOnline) runs the
+// items only when no head takes the bound loop, else the second does.
+enum { kGateNone = 0, kGateOnline = 1 };
+
 // One work item w (a query tile of one (batch, head)) on the softmax path
 // BOUND, in the stage array `smem`.  Returns kDeclined, having written
 // nothing, when the item takes the other path; kRetry, having written
@@ -1141,7 +1155,7 @@ enum ItemResult { kDeclined = 0, kDone = 1, kRetry = 2 };
 // valid item).  All waves of the workgroup call it and return together,
 // except that waves with no rows may return before the epilogue.  Only
 // kernels built with CHECK (launched for mode 5) hold the check.
-template <int D, int NQB, int NW, bool BOUND, bool MASK, bool CHECK>
+template <int D, int NQB, int NW, bool BOUND, bool MASK, bool CHECK, bool NODECLINE = false>
 __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, const ci32* kv_ptr,
                                         const ci32* kv_iv, const cf32* k_gmax, const cf32* head_max,
                                         u16* smem, int w, bool force_online = false) {
@@ -1186,9 +1200,12 @@ __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, c
   if (a.mode == ATTN_SOFTMAX_BOUND_FORCED) {
     path = kPre;
   } else if (a.mode == ATTN_SOFTMAX_BOUND || a.mode == ATTN_SOFTMAX_BOUND_EXACT) {
-    const float mq = head_max[2 * bh], mk = head_max[2 * bh + 1];
-    path = classify(2.0f * a.scale * mq * mk);
-    if (a.mode == ATTN_SOFTMAX_BOUND_EXACT && path == kPre) path = kExact;  // never rounds Q
+    path = classify(head_slack(a.scale, head_max, bh));
+    // Mode 4 never rounds Q.  Nor does a kernel with no bound loop to hand
+    // the item to (the online-only persistent kernel, NODECLINE): in mode 1
+    // it runs only when no head takes the bound loop, and should one still
+    // test so, it keeps Q exact rather than leave the item undone.
+    if ((a.mode == ATTN_SOFTMAX_BOUND_EXACT || NODECLINE) && path == kPre) path = kExact;
   }
   if (!per_tile && (path == kPre) != BOUND) return kDeclined;
 
@@ -1435,6 +1452,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   // [0]: the item index; [1] (CHECK): 1 while the item is to run again.
   int32_t* const item_word = reinterpret_cast<int32_t*>(smem + kBuffers * C::STAGE);
   uint32_t empty = 0;  // thread 0: the queues found exhausted
+  if constexpr (!BOTH) {
+    // Gated (mode 1, launched before the combined kernel): when some head
+    // takes the bound loop, leave every item to the combined kernel,
+    // touching nothing.  Every wave tests every head (one per lane), so all
+    // reach the same answer without a barrier.
+    const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(args));
+    const kernarg_args& ka = *reinterpret_cast<const kernarg_args*>(args);
+    if (ka.gate == kGateOnline) {
+      const cf32* hm = (const cf32*)ka.head_max;
+      bool bound = false;
+      for (int bh = threadIdx.x & 63; bh < ka.B * ka.H; bh += 64)
+        bound |= head_slack(ka.scale, hm, bh) <= ATTN_PRESCALE_NATS;
+      if (__any(bound)) return;
+    }
+  }
   if constexpr (CHECK) {
     if (threadIdx.x == 0) item_word[1] = 0;  // (read after the loop's first barrier)
   }
@@ -1488,9 +1521,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
       FwdArgs ib;
       item_args(ib);
       const bool force = CHECK && __builtin_amdgcn_readfirstlane(item_word[1]) != 0;
-      const int r = run_item<D, NQB, NW, false, MASK, CHECK>(ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr,
-                                                             (const ci32*)ib.kv_iv, (const cf32*)ib.k_gmax,
-                                                             (const cf32*)ib.head_max, smem, w, force);
+      const int r = run_item<D, NQB, NW, false, MASK, CHECK, !BOTH>(
+          ib, (const ci32*)ib.q_tiles, (const ci32*)ib.kv_ptr, (const ci32*)ib.kv_iv, (const cf32*)ib.k_gmax,
+          (const cf32*)ib.head_max, smem, w, force);
       if constexpr (CHECK) {
         // (both cases walked the tile, past barriers that follow every
         // wave's reads of the flag)
@@ -1501,16 +1534,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   // Leaving: work_ctr[n_xcd] counts the workgroups that are done.  The last
   // one (every other workgroup has made its last slot request, as it counts
   // itself only after them) sets all counters back to zero for the next call
-  // on this workspace.
+  // on this workspace -- or, after a gated online-only launch that ran the
+  // items, every queue counter to its depth: the combined kernel launched
+  // next then finds every queue exhausted, and its last workgroup zeroes them.
   if (threadIdx.x == 0) {
     const kernarg_char* args = (const kernarg_char*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(args));
     const kernarg_args& ka = *reinterpret_cast<const kernarg_args*>(args);
     int32_t* counters = ka.work_ctr;
     const int nx = ka.n_xcd;
+    const int left = !BOTH && ka.gate == kGateOnline ? ka.n_work / nx : 0;
     // (atomic writes: the next call's slot requests may come from other dies)
     if (atomicAdd(counters + nx, 1) == (int)gridDim.x - 1)
-      for (int x = 0; x <= nx; ++x) atomicExch(counters + x, 0);
+      for (int x = 0; x <= nx; ++x) atomicExch(counters + x, x < nx ? left : 0);
   }
 }
 
@@ -1528,10 +1564,22 @@ int launch_persistent(const FwdArgs& a, int grid, bool both, bool check, hipStre
       return ok();
     }
   }
-  if (both)
+  if (both && a.mode == ATTN_SOFTMAX_BOUND) {
+    // Per-head mode: when no head takes the bound loop, the online-only
+    // kernel runs every item (the online loop of the combined kernel runs a
+    // few per cent slower) and leaves the queues exhausted for the combined
+    // kernel; otherwise it leaves at once and the combined kernel runs them.
+    FwdArgs g = a;
+    g.gate = kGateOnline;
+    hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, false, false>), dim3(grid), dim3(64 * NW), 0, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
     hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
-  else
+  } else if (both) {
+    hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, true, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  } else {
     hipLaunchKernelGGL((fwd_persistent<D, NQB, NW, MASK, false, false>), dim3(grid), dim3(64 * NW), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(ATTN_E_HIP, std::string("launch failed: ") + hipGetErrorString(e));
   return ok();
@@ -1680,6 +1728,7 @@ static int fwd_entry(const void* q, const void* k, const void* v, void* o, float
   a.k_gmax = k_gmax;
   a.head_max = head_max;
   a.mode = softmax_mode;
+  a.gate = kGateNone;
   const bool check = softmax_mode == ATTN_SOFTMAX_BOUND_CHECKED;
   a.head_path_out = head_path_out;
   a.kv_flag = kv_flag;

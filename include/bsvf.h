@@ -270,7 +270,14 @@ typedef struct attn_blocks_t {
                                 from the others', counting handed-out slots
                                 here: dies that run faster take over the slower
                                 ones' work, and online items share the CUs with
-                                bound ones.  The caller zeroes it once before its
+                                bound ones.  (In mode 1 the launch is two
+                                kernels in a row on the stream: one holding
+                                both loops and one holding the online loop
+                                alone, with its own register allocation; each
+                                first tests the head norms on the device, and
+                                only the second takes items when no head
+                                passes with the prescaled Q, only the first
+                                otherwise.)  The caller zeroes it once before its
                                 first use; every call leaves it zero again.
                                 Calls that share it must not overlap (one
                                 stream, or a stream that waits for the other

@@ -555,6 +555,40 @@ def test_persistent_launch_any_queue_layout(num_xcd, group, mode):
         assert not blk.work_ctr.cpu().numpy().any()
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_per_head_mode_runs_one_kernel(D):
+    """Mode 1's persistent launch is two kernels, the combined one and the
+    online-only one, of which exactly one takes items, chosen on the device
+    from the head norms: with every head beyond the per-head limit (Q scaled
+    up) the bits equal mode 0's and every head reports the online path; with
+    every head within it they equal the static launch's.  Two calls each, and
+    the slot counters are zero after every call."""
+    import torch
+    from gpu_util import to_device
+    p, B, H = Pattern(5, 304, 1, 1, (0,)), 1, 3
+    scale = 1.0 / math.sqrt(D)
+    q0, k, v = random_qkv(B, H, p.seq_len, D, seed=13)
+    for qmul, want_path in ((8.0, 0), (1.0, 1)):
+        q = f32_to_bf16_bits(bf16_bits_to_f32(q0) * np.float32(qmul))
+        hm = ON.head_max(ON.row_norms(q), ON.row_norms(k))
+        sl = ON.slack_bound(hm, scale)
+        assert (sl > ON.ELIGIBLE_NATS).all() if want_path == 0 else (sl < bs.PRESCALE_NATS).all(), sl
+        ref = run_gpu(q, k, v, p, scale, bs.SOFTMAX_ONLINE if want_path == 0 else bs.SOFTMAX_BOUND,
+                      persistent=want_path == 0)
+        qd, kd, vd = to_device(q), to_device(k), to_device(v)
+        blk = bs.build_blocks_for(p, 256).to_device(torch.device("cuda"), B, H)
+        assert blk.work_ctr is not None
+        nm = bs.norms(qd, kd)
+        for _ in range(2):
+            hp = torch.full((B, H), -1, dtype=torch.int32, device="cuda")
+            o, lse = bs.attention(qd, kd, vd, blk, scale, bs.SOFTMAX_BOUND, norms=nm, head_path=hp)
+            torch.cuda.synchronize()
+            assert o.contiguous().view(torch.int16).cpu().numpy().tobytes() == ref["o_bytes"]
+            assert lse.cpu().numpy().tobytes() == ref["lse_bytes"]
+            assert (hp.cpu().numpy() == want_path).all()
+            assert not blk.work_ctr.cpu().numpy().any()
+
+
 def _checked_inputs(D):
     """N(0,1) draws with every Q row scaled by exp(0.35 z) and every key
     shifted by 3 along the first axis; frame 3's query rows point against that
