@@ -31,22 +31,26 @@ from collections import defaultdict
 
 
 def short_name(kernel: str) -> str:
-    # fwd_persistent<D, NQB, NW, MASK, BOTH>: one workgroup per CU, each item
-    # on its own softmax path (BOTH), or the online path alone
+    # fwd_persistent<D, NQB, NW, MASK, BOTH, CHECK>: one workgroup per CU,
+    # each item on its own softmax path (BOTH), or the online path alone; the
+    # CHECK kernels run mode 5
     m = re.search(r"fwd_persistent<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         masked = len(args) > 3 and args[3] == "true"
         online = len(args) > 4 and args[4] == "false"
-        return f"attn_fwd[persistent{',online' if online else ''}{',masked' if masked else ''}]"
-    # fwd_kernel<D, NQB, NW, BOUND, MASK>: one workgroup per item, reported
-    # under the path it runs
+        checked = len(args) > 5 and args[5] == "true"
+        return (f"attn_fwd[persistent{',online' if online else ''}{',masked' if masked else ''}"
+                f"{',checked' if checked else ''}]")
+    # fwd_kernel<D, NQB, NW, BOUND, MASK, CHECK>: one workgroup per item,
+    # reported under the path it runs
     m = re.search(r"fwd_kernel<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]
         path = "bound" if len(args) > 3 and args[3] == "true" else "online"
         masked = len(args) > 4 and args[4] == "true"
-        return f"attn_fwd[{path}{',masked' if masked else ''}]"
+        checked = len(args) > 5 and args[5] == "true"
+        return f"attn_fwd[{path}{',masked' if masked else ''}{',checked' if checked else ''}]"
     m = re.search(r"prep_kernel<([^>]*)>", kernel)
     if m:
         args = [x.strip() for x in m.group(1).split(",")]

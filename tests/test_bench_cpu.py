@@ -49,6 +49,14 @@ def test_kernel_short_names():
         == "attn_fwd[persistent,masked]"
     assert short_name(ns + "fwd_persistent<128, 1, 8, false, false>(bsvf::(anonymous namespace)::FwdArgs)") \
         == "attn_fwd[persistent,online]"
+    assert short_name(ns + "fwd_persistent<128, 1, 8, false, true, false>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[persistent]"
+    assert short_name(ns + "fwd_persistent<128, 1, 8, false, false, false>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[persistent,online]"
+    assert short_name(ns + "fwd_persistent<64, 1, 8, false, true, true>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[persistent,checked]"
+    assert short_name(ns + "fwd_kernel<128, 1, 8, false, false, true>(bsvf::(anonymous namespace)::FwdArgs)") \
+        == "attn_fwd[online,checked]"
     assert short_name(ns + "fwd_kernel<128, 1, 8, true, false>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
         == "attn_fwd[bound]"
     assert short_name(ns + "fwd_kernel<64, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
