@@ -27,19 +27,22 @@
  *     been written and nothing launched; attn_last_error() gives a message
  *     (per calling thread).
  *   - Every buffer is owned by the caller.  The library allocates no memory
- *     and keeps no state of its own between calls; it never synchronizes.
+ *     and, apart from attn_fwd_noalloc's counter array (below), keeps no
+ *     state of its own between calls; it never synchronizes.
  *     Device work is enqueued on the caller's stream and the call returns at
  *     once.  A device fault surfaces at the caller's next synchronization.
- *     The one piece of state that outlives a call is the caller-given
- *     workspace attn_blocks_t.work_ctr (counters every call leaves zero).
+ *     The other state that outlives a call is the caller-given workspace
+ *     attn_blocks_t.work_ctr (counters every call leaves zero).
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary CPU memory.
  *   - bf16 tensors are passed as const void* to raw 16-bit bf16 storage.
- *   - The library holds no global mutable state, so calls from several
- *     threads are safe as long as they share no output buffer and no
- *     work_ctr workspace: calls that share a workspace must be ordered (one
- *     stream, or a stream that waits on the other's work), because each call
- *     hands out its work through those counters and resets them at its end.
+ *   - Besides that array (one per GPU, shared by every attn_fwd_noalloc
+ *     call on it) the library holds no global mutable state, so calls from
+ *     several threads are safe as long as they share no output buffer and no
+ *     work_ctr workspace, and attn_fwd_noalloc calls on one GPU do not
+ *     overlap: calls that share counters must be ordered (one stream, or a
+ *     stream that waits on the other's work), because each call hands out
+ *     its work through those counters and resets them at its end.
  */
 #ifndef BSVF_H
 #define BSVF_H
