@@ -1437,9 +1437,10 @@ __device__ __forceinline__ void item_args(FwdArgs& ia) {
 // having written nothing, when the item takes the online path, which then
 // runs it.  So online items (whole heads in mode 1, single tiles in mode 3)
 // fill the same CUs as the bound ones instead of following them in a launch
-// of their own.  Without BOTH the kernel holds the online path alone (the
-// online mode): sharing a kernel with the bound path costs the online loop
-// about 2%.  The outputs do not depend on which workgroup computes an item.
+// of their own.  Without BOTH the kernel holds the online path alone (modes
+// 0 and 4, and in mode 1 the gated launch before the combined kernel):
+// sharing a kernel with the bound path costs the online loop a few per
+// cent.  The outputs do not depend on which workgroup computes an item.
 template <int D, int NQB, int NW, bool MASK, bool BOTH, bool CHECK>
 __global__ __launch_bounds__(64 * NW) void fwd_persistent(FwdArgs a) {
   (void)a;  // read through the argument-segment pointer below
