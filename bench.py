@@ -261,7 +261,7 @@ def cpu_baseline(wl, q, k, v, target_s: float):
                   or g in wl.pattern.global_frames]
         return len(frames) * T
 
-    chunk = 512
+    chunk = min(512, wl.seq_len)
 
     def task(h, rows):
         OA.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], wl.pattern, wl.scale, rows=rows, chunk=chunk)

@@ -62,3 +62,15 @@ def test_kernel_short_names():
     assert short_name(ns + "fwd_kernel<64, 1, 8, false, true>(bsvf::(anonymous namespace)::FwdArgs, int const*)") \
         == "attn_fwd[online,masked]"
     assert short_name(ns + "head_max_kernel<true>(float const*, float const*, int, float*)") == "attn_norms[head_max]"
+
+
+def test_cpu_baseline_pool_on_the_tiny_workload():
+    """The CPU baseline runs the oracle in a pool of one worker per host core
+    over (head, 512-row) tasks and reports the workers as its cores."""
+    from synth import WORKLOADS, make_qkv
+    wl = WORKLOADS["tiny"]
+    q, k, v = make_qkv(wl)
+    r = bench.cpu_baseline(wl, q, k, v, 0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] == r["workers"] == r["host_cores"] == len(os.sched_getaffinity(0))
+    assert f"{wl.seq_len} rows" in r["sample"]   # a task holds min(512, N) rows
