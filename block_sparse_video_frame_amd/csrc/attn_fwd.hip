@@ -47,6 +47,7 @@
 
 #include <cfloat>
 #include <mutex>
+#include <type_traits>
 
 namespace bsvf {
 namespace {
@@ -166,6 +167,12 @@ __device__ __forceinline__ bool interval_ok(int ks, int kl, int N) {
   return ks >= 0 && kl > 0 && ((ks | kl) & 15) == 0 && ks <= N - kl;
 }
 
+// Stages in flight ahead of the one being consumed, and LDS buffers: the
+// prefetch window, the stage being consumed, and the lagging half's previous
+// stage (see run_tile).
+constexpr int kPrefetch = 2;
+constexpr int kBuffers = kPrefetch + 2;
+
 template <int D, int NQB, int NW>
 struct Cfg {
   static constexpr int NT = 64 * NW;
@@ -175,6 +182,13 @@ struct Cfg {
   static constexpr int DBLK = D / 32;            // 32-wide output blocks
   static constexpr int REGION = BK * D;          // elements of K (or V) per stage
   static constexpr int STAGE = 2 * REGION;       // K + V elements per stage
+  // Stage buffer x's K region starts BSTRIDE * x elements into the stage
+  // array and its V region VOFF elements past its K.  At D = 128 a buffer is
+  // K then V; at D = 64 the four K regions come first, then the four V
+  // regions, so every buffer's offset within the K (or V) regions fits a
+  // read's immediate offset (see Tile::kImm).
+  static constexpr int BSTRIDE = D == 64 ? REGION : STAGE;
+  static constexpr int VOFF = D == 64 ? kBuffers * REGION : REGION;
   static constexpr int LPW = DC / NW;            // 1 KiB direct loads per wave per region
   static_assert(LPW >= 1 && LPW * NW == DC, "tile shape");
 };
@@ -276,7 +290,7 @@ __device__ __forceinline__ void issue_stage_run(u16* ks, __amdgpu_buffer_rsrc_t 
   for (int it = 0; it < C::LPW; ++it) {
     const int blk = it * NW + wave;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + blk * 512), 16, (int)dl.k[it], (int)sk, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::REGION + blk * 512), 16, (int)dl.v[it],
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::VOFF + blk * 512), 16, (int)dl.v[it],
                                              (int)sv, 0, 0);
   }
 }
@@ -309,7 +323,7 @@ __device__ __forceinline__ void issue_stage(u16* ks, __amdgpu_buffer_rsrc_t kr, 
     const int base = r < sd.end[0] ? sd.base[0] : r < sd.end[1] ? sd.base[1] : r < sd.end[2] ? sd.base[2] : sd.base[3];
     const uint32_t key = base + r;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(ks + blk * 512), 16, 2 * (key * ksn + col), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::REGION + blk * 512), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(ks + C::VOFF + blk * 512), 16,
                                              2 * (key * vsn + col), 0, 0, 0);
   }
 }
@@ -365,10 +379,44 @@ struct Tile {
   int fq[NQB];  // frame of this lane's query row (frame-unaware layout only)
   LaneOffsets<D> lof;
   static constexpr uint32_t RS = 2 * D;
+  // At D = 64 the K operand addresses within a buffer live in registers, one
+  // per k-step: kx[st] = kl ^ 32st.  A buffer's byte offset `boff` (a
+  // multiple of the region size, above these bits) then adds as the read's
+  // immediate offset wherever the walk knows the buffer at compile time (see
+  // run_tile), so such a read needs no address arithmetic.  (At D = 128 the
+  // eight registers are not to be had: each read forms its address with one
+  // XOR.)
+  static constexpr bool kImm = D == 64;
+  uint32_t kx[kImm ? C::KSTEPS : 1];
+  __device__ __forceinline__ void set_addresses() {
+    if constexpr (kImm) {
+#pragma unroll
+      for (int st = 0; st < C::KSTEPS; ++st) kx[st] = lof.kl ^ (32u * st);
+    }
+  }
+  // Called at the top of each step: the per-lane offsets count as new values
+  // there, so the compiler does not hoist offset-plus-buffer sums for every
+  // buffer out of the walk (which would hold one register per sum).
+  __device__ __forceinline__ void renew_addresses() {
+    if constexpr (kImm) {
+#pragma unroll
+      for (int st = 0; st < C::KSTEPS; ++st) asm volatile("" : "+v"(kx[st]));
+      asm volatile("" : "+v"(lof.vl[0]), "+v"(lof.vl[1]));
+    }
+  }
+
+  // Byte address (less v_rows()) of the transposing V reads of output block
+  // db, lane half `hi`, in the stage buffer at byte `boff`.
+  __device__ __forceinline__ uint32_t v_address(uint32_t boff, int hi, int db) const {
+    if constexpr (kImm) return ((boff + 2u * C::VOFF) | (64u * db)) ^ lof.vl[hi];
+    else return boff | (lof.vl[hi] ^ (64u * db));
+  }
+  __device__ __forceinline__ static constexpr uint32_t v_rows() { return kImm ? 0u : 2u * C::VOFF; }
 
   // K operand of block kb, k-step st, of the stage buffer at byte `boff`.
   __device__ __forceinline__ bf16x8 k_operand(const lds_char* sm, uint32_t boff, int kb, int st) const {
-    return *(const volatile lds_bf16x8*)(sm + (((boff | lof.kl) ^ (32u * st)) + 32u * RS * kb));
+    if constexpr (kImm) return *(const volatile lds_bf16x8*)(sm + kx[st] + (boff + 32u * RS * kb));
+    else return *(const volatile lds_bf16x8*)(sm + (((boff | lof.kl) ^ (32u * st)) + 32u * RS * kb));
   }
 
   // Score accumulators start at acc0[qb]: the bound loop starts at -m (its Q
@@ -676,14 +724,14 @@ struct Tile {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) va[h2][db] = boff | (lof.vl[h2] ^ (64u * db));
+      for (int db = 0; db < C::DBLK; ++db) va[h2][db] = v_address(boff, h2, db);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db) {
-          const uint32_t rows = C::REGION * 2 + RS * (32 * kb + 16 * kst);
+          const uint32_t rows = v_rows() + RS * (32 * kb + 16 * kst);
           const i16x4 lo4 = ds_read_tr16(sm + va[0][db] + rows);
           const i16x4 hi4 = ds_read_tr16(sm + va[1][db] + rows);
           const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -774,8 +822,8 @@ struct Tile {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int db = 0; db < C::DBLK; ++db) va[h2][db] = boff | (lof.vl[h2] ^ (64u * db));
-    const uint32_t base = C::REGION * 2 + RS * 32 * kb;
+      for (int db = 0; db < C::DBLK; ++db) va[h2][db] = v_address(boff, h2, db);
+    const uint32_t base = v_rows() + RS * 32 * kb;
 #pragma unroll
     for (int kst = 0; kst < 2; ++kst)
 #pragma unroll
@@ -797,11 +845,6 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) |
 #ifndef ISSUE_LAG
 #define ISSUE_LAG 1
 #endif
-// Stages in flight ahead of the one being consumed, and LDS buffers: the
-// prefetch window, the stage being consumed, and the lagging half's previous
-// stage (see run_tile).
-constexpr int kPrefetch = 2;
-constexpr int kBuffers = kPrefetch + 2;
 
 // Cuts the tile's valid intervals into consecutive 64-key stages (scalar,
 // uniform state).  Intervals outside [0, N) or not 16-aligned are skipped.
@@ -915,9 +958,10 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
     if (interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) total += kv_iv[2 * e + 1];
   if (total == 0) return;
   const int ns = (total + BK - 1) / BK, nlast = total - BK * (ns - 1);
-  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::STAGE; };
-  // byte offset of stage x's buffer within smem (K at +0, V at +2*REGION)
-  auto boff = [&](int x) { return (uint32_t)((x & (kBuffers - 1)) * C::STAGE * 2); };
+  // stage x's K region (its V region lies VOFF elements on)
+  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::BSTRIDE; };
+  // byte offset of stage x's K region within the stage array
+  auto boff = [&](int x) { return (uint32_t)((x & (kBuffers - 1)) * C::BSTRIDE * 2); };
   const lds_char* sm = lds_bytes(smem);
   KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
   kw.seek();
@@ -952,7 +996,18 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
   if (active) T.scores(sm, boff(0), sc);
   typename TT::Probs pk;
   float alpha[NQB];
-  auto step = [&](int st, typename TT::Scores& cur, typename TT::Scores& nxt) {
+  // A step's buffers: stage st + rel is in buffer (st + rel) mod kBuffers.
+  // The walk below runs the steps in groups of kBuffers with st a multiple of
+  // kBuffers at the first (Phase J is st mod kBuffers, or -1 where unknown),
+  // so the buffer offsets are compile-time constants that the operand reads
+  // take as immediate offsets.
+  auto step = [&](auto phase, int st, typename TT::Scores& cur, typename TT::Scores& nxt) {
+    constexpr int J = decltype(phase)::value;
+    T.renew_addresses();
+    auto bo = [&](int rel) -> uint32_t {
+      if constexpr (J >= 0) return (uint32_t)(((J + rel) & (kBuffers - 1)) * C::BSTRIDE * 2);
+      else return boff(st + rel);
+    };
     // Stage st+1 has landed (every wave): at most the stages after it are
     // still in flight.  Every wave is also done with the buffer stage
     // st+kPrefetch is about to overwrite.
@@ -972,7 +1027,7 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
     mask_stage(cur, st);
     if constexpr (LAG) {
       if (st > 0) {
-        T.pv(sm, boff(st - 1), pk);
+        T.pv(sm, bo(-1), pk);
         pin_pv<4 * C::DBLK * NQB>();
       }
       if constexpr (ISSUE_LAG) {
@@ -980,23 +1035,37 @@ __device__ __forceinline__ void run_tile(const FwdArgs& a, const ci32* kv_iv, u1
         if (more) issue(st + kPrefetch);
         __builtin_amdgcn_sched_barrier(0);
       }
-      T.template softmax_and_scores<BOUND>(cur, sm, boff(st + 1), nxt, pk, alpha, a.c2);
+      T.template softmax_and_scores<BOUND>(cur, sm, bo(1), nxt, pk, alpha, a.c2);
       if constexpr (!BOUND) T.rescale(alpha);
     } else {
-      T.template softmax_and_scores<BOUND>(cur, sm, boff(st + 1), nxt, pk, alpha, a.c2);
+      T.template softmax_and_scores<BOUND>(cur, sm, bo(1), nxt, pk, alpha, a.c2);
       if constexpr (!BOUND) T.rescale(alpha);
-      T.pv(sm, boff(st), pk);
+      T.pv(sm, bo(0), pk);
       pin_pv<4 * C::DBLK * NQB>();
     }
   };
   typename TT::Scores sn;
+  static_assert(kBuffers == 4, "the walk runs its steps in groups of four");
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  using PX = std::integral_constant<int, -1>;
   int st = 0;
+  if constexpr (TT::kImm) {
+    for (; st + 4 < ns; st += 4) {
+      step(P0{}, st, sc, sn);
+      step(P1{}, st + 1, sn, sc);
+      step(P2{}, st + 2, sc, sn);
+      step(P3{}, st + 3, sn, sc);
+    }
+  }
   for (; st + 2 < ns; st += 2) {
-    step(st, sc, sn);
-    step(st + 1, sn, sc);
+    step(PX{}, st, sc, sn);
+    step(PX{}, st + 1, sn, sc);
   }
   if (st + 1 < ns) {
-    step(st, sc, sn);
+    step(PX{}, st, sc, sn);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1040,8 +1109,8 @@ __device__ __forceinline__ void run_thin(const FwdArgs& a, const ci32* kv_iv, u1
     if (interval_ok(kv_iv[2 * e], kv_iv[2 * e + 1], a.N)) total += kv_iv[2 * e + 1];
   if (total == 0) return;
   const int ns = (total + BK - 1) / BK, nlast = total - BK * (ns - 1);
-  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::STAGE; };
-  auto boff = [&](int x) { return (uint32_t)((x & (kBuffers - 1)) * C::STAGE * 2); };
+  auto kbuf = [&](int x) { return smem + (x & (kBuffers - 1)) * C::BSTRIDE; };
+  auto boff = [&](int x) { return (uint32_t)((x & (kBuffers - 1)) * C::BSTRIDE * 2); };
   const lds_char* sm = lds_bytes(smem);
   KeyWalker kw{kv_iv, e0, e1, a.N, 0, 0, 0, false};
   kw.seek();
@@ -1256,6 +1325,7 @@ __device__ __forceinline__ int run_item(const FwdArgs& a, const ci32* q_tiles, c
   T.hh = lane >> 5;
   T.lane = lane;
   T.lof = lane_offsets<D>(lane);
+  T.set_addresses();
   // A tile of at most 64 rows runs thin (see run_thin): waves 4g to 4g+3
   // all hold row group g.
   bool thin = false;
