@@ -379,8 +379,9 @@ struct Tile {
   int fq[NQB];  // frame of this lane's query row (frame-unaware layout only)
   LaneOffsets<D> lof;
   static constexpr uint32_t RS = 2 * D;
-  // At D = 64 the K operand addresses within a buffer live in registers, one
-  // per k-step: kx[st] = kl ^ 32st.  A buffer's byte offset `boff` (a
+  // At D = 64 the operand addresses within a buffer live in registers: the K
+  // operand of k-step st at kx[st] = kl ^ 32st, the transposing V reads of
+  // output block db at vx[hi][db] (from the start of the V regions).  A buffer's byte offset `boff` (a
   // multiple of the region size, above these bits) then adds as the read's
   // immediate offset wherever the walk knows the buffer at compile time (see
   // run_tile), so such a read needs no address arithmetic.  (At D = 128 the
@@ -388,10 +389,15 @@ struct Tile {
   // XOR.)
   static constexpr bool kImm = D == 64;
   uint32_t kx[kImm ? C::KSTEPS : 1];
+  uint32_t vx[2][kImm ? C::DBLK : 1];
   __device__ __forceinline__ void set_addresses() {
     if constexpr (kImm) {
 #pragma unroll
       for (int st = 0; st < C::KSTEPS; ++st) kx[st] = lof.kl ^ (32u * st);
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) vx[hi][db] = 2u * C::VOFF + (lof.vl[hi] ^ (64u * db));
     }
   }
   // Called at the top of each step: the per-lane offsets count as new values
@@ -401,14 +407,17 @@ struct Tile {
     if constexpr (kImm) {
 #pragma unroll
       for (int st = 0; st < C::KSTEPS; ++st) asm volatile("" : "+v"(kx[st]));
-      asm volatile("" : "+v"(lof.vl[0]), "+v"(lof.vl[1]));
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) asm volatile("" : "+v"(vx[hi][db]));
     }
   }
 
   // Byte address (less v_rows()) of the transposing V reads of output block
   // db, lane half `hi`, in the stage buffer at byte `boff`.
   __device__ __forceinline__ uint32_t v_address(uint32_t boff, int hi, int db) const {
-    if constexpr (kImm) return ((boff + 2u * C::VOFF) | (64u * db)) ^ lof.vl[hi];
+    if constexpr (kImm) return boff + vx[hi][db];
     else return boff | (lof.vl[hi] ^ (64u * db));
   }
   __device__ __forceinline__ static constexpr uint32_t v_rows() { return kImm ? 0u : 2u * C::VOFF; }
