@@ -381,12 +381,13 @@ struct Tile {
   static constexpr uint32_t RS = 2 * D;
   // At D = 64 the operand addresses within a buffer live in registers: the K
   // operand of k-step st at kx[st] = kl ^ 32st, the transposing V reads of
-  // output block db at vx[hi][db] (from the start of the V regions).  A buffer's byte offset `boff` (a
-  // multiple of the region size, above these bits) then adds as the read's
-  // immediate offset wherever the walk knows the buffer at compile time (see
-  // run_tile), so such a read needs no address arithmetic.  (At D = 128 the
-  // eight registers are not to be had: each read forms its address with one
-  // XOR.)
+  // output block db at vx[hi][db] (from the start of the V regions).  A
+  // buffer's byte offset `boff` (a multiple of the region size, above these
+  // bits) then adds as the read's immediate offset wherever the walk knows
+  // the buffer at compile time (see run_tile), so such a read needs no
+  // address arithmetic.  At D = 128 each read forms its address with one XOR:
+  // the twelve registers would spill in the combined kernel, and the XORs hide
+  // under the stage's matrix work there.
   static constexpr bool kImm = D == 64;
   uint32_t kx[kImm ? C::KSTEPS : 1];
   uint32_t vx[2][kImm ? C::DBLK : 1];
