@@ -513,6 +513,29 @@ def _random_case(i):
     return Pattern(F, T, before, after, g), 1, H, D, bq
 
 
+@pytest.mark.parametrize("stages", list(range(2, 13)))
+def test_d64_walk_every_stage_count(stages):
+    """At D = 64 the walk runs its steps in groups of four, each with its
+    buffer offsets fixed at compile time, then the rest two by two.  One
+    frame of 64 * stages - 48 tokens attended frame-locally gives 256-row
+    tiles (and the last, shorter tile) 2 to 12 stages of keys, the last one
+    16 keys: every count of leftover steps after the groups of four.  All rows
+    against the oracle in modes 0 and 1; the persistent and the static launch
+    give the same bits."""
+    T = 64 * stages - 48
+    p = Pattern(1, T, 0, 0)
+    q, k, v = random_qkv(1, 2, T, 64, seed=7000 + stages)
+    scale = 0.125
+    O, L = OA.attention(q, k, v, p, scale)
+    for mode in (bs.SOFTMAX_ONLINE, bs.SOFTMAX_BOUND):
+        a = run_gpu(q, k, v, p, scale, mode)
+        b = run_gpu(q, k, v, p, scale, mode, persistent=False)
+        e = errors(a["o"], a["lse"], O, L)
+        record("d64_walk_every_stage_count", str(stages), mode, e)
+        assert within(e), (stages, mode, e)
+        assert a["o_bytes"] == b["o_bytes"] and a["lse_bytes"] == b["lse_bytes"], (stages, mode)
+
+
 @pytest.mark.parametrize("case", range(24))
 def test_random_patterns_all_rows(case):
     p, B, H, D, bq = _random_case(case)
